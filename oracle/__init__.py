@@ -1,0 +1,6 @@
+"""CPU oracle (test infrastructure only; never on the product path)."""
+from .qoq_oracle import *  # noqa: F401,F403
+from .qoq_oracle import (PROTECT, ACT_MAX, Q4_MAX, rne_div, ceil_div,  # noqa: F401
+                         level1_per_channel, level2_per_group, dequantize_level2,
+                         quantize_weights, quantize_act, int_gemm, int_gemm_fp64,
+                         epilogue, w4a8_linear)

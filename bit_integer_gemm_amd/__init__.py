@@ -1,0 +1,253 @@
+"""Python binding of libqoq (QoQ W4A8 GEMM for MI355X / gfx950).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every computation runs in the HIP kernels of
+``libqoq.so``. There is no CPU fallback: if the library is missing or no GPU
+is visible the calls raise.
+
+Low-level names mirror the C ABI in include/qoq.h (``qoq_pack_weights``,
+``qoq_quantize_act``, ``qoq_w4a8_gemm``, ``qoq_packed_weight_bytes``,
+``qoq_gemm_workspace_bytes``, ``qoq_status_string``); ``pack_weights``,
+``quantize_act`` and ``w4a8_gemm`` are the tensor-level conveniences.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "QoQError", "lib", "GROUP", "PACK_FROM_CANONICAL",
+    "qoq_packed_weight_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
+    "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string",
+    "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
+    "Workspace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
+GROUP = 128
+PACK_FROM_CANONICAL = 0x1
+
+QOQ_STATUS = {
+    0: "QOQ_OK", 1: "QOQ_ERR_NULL", 2: "QOQ_ERR_SHAPE", 3: "QOQ_ERR_ALIGN",
+    4: "QOQ_ERR_GROUP", 5: "QOQ_ERR_WORKSPACE", 6: "QOQ_ERR_HIP", 7: "QOQ_ERR_FLAGS",
+}
+
+
+class QoQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {QOQ_STATUS.get(status, status)} "
+                         f"({qoq_status_string(status)})")
+
+
+class _Canonical(ctypes.Structure):
+    _fields_ = [("q4", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("z", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqoq.so (built in-tree by ``python -m bit_integer_gemm_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_integer_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_uint32, ctypes.c_size_t)
+        L.qoq_packed_weight_bytes.argtypes = [i64, i64, i32]
+        L.qoq_packed_weight_bytes.restype = sz
+        L.qoq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.qoq_gemm_workspace_bytes.restype = sz
+        L.qoq_pack_weights.argtypes = [vp, i64, i64, i32, vp, vp, ctypes.POINTER(_Canonical),
+                                       u32, vp]
+        L.qoq_pack_weights.restype = ctypes.c_int
+        L.qoq_quantize_act.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.qoq_quantize_act.restype = ctypes.c_int
+        L.qoq_w4a8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
+        L.qoq_w4a8_gemm.restype = ctypes.c_int
+        L.qoq_status_string.argtypes = [ctypes.c_int]
+        L.qoq_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------------------
+# C-ABI mirrors (raw pointers as ints; stream as an int handle or None)
+# ---------------------------------------------------------------------------
+def qoq_status_string(status: int) -> str:
+    return lib().qoq_status_string(int(status)).decode()
+
+
+def qoq_packed_weight_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return int(lib().qoq_packed_weight_bytes(N, K, group))
+
+
+def qoq_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().qoq_gemm_workspace_bytes(M, N, K))
+
+
+def qoq_pack_weights(W, N, K, group, packed, s1, canon, flags, stream) -> int:
+    c = None
+    if canon is not None:
+        c = ctypes.byref(_Canonical(*canon))
+    return lib().qoq_pack_weights(W, N, K, group, packed, s1, c, flags, stream)
+
+
+def qoq_quantize_act(x, M, K, x8, s_x, stream) -> int:
+    return lib().qoq_quantize_act(x, M, K, x8, s_x, stream)
+
+
+def qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
+                  workspace_bytes, stream) -> int:
+    return lib().qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
+                               workspace_bytes, stream)
+
+
+# ---------------------------------------------------------------------------
+# tensor-level helpers
+# ---------------------------------------------------------------------------
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QoQError(status, where)
+
+
+def _need_gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedWeight:
+    packed: torch.Tensor          # uint8 [qoq_packed_weight_bytes]
+    s1: torch.Tensor              # float16 [N]
+    N: int
+    K: int
+    group: int = GROUP
+    q4: Optional[torch.Tensor] = None   # canonical outputs when requested
+    s2: Optional[torch.Tensor] = None
+    z: Optional[torch.Tensor] = None
+
+
+def pack_weights(W: torch.Tensor, group: int = GROUP, canonical: bool = False) -> PackedWeight:
+    """Quantize W fp32 [N, K] (device) in two levels and pack it."""
+    _need_gpu(W, "W", torch.float32)
+    N, K = W.shape
+    nbytes = qoq_packed_weight_bytes(N, K, group)
+    if nbytes == 0:
+        raise QoQError(2, "qoq_pack_weights")
+    dev = W.device
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s1 = torch.empty(N, dtype=torch.float16, device=dev)
+    canon = None
+    q4 = s2 = z = None
+    if canonical:
+        q4 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((N, K // group), dtype=torch.int8, device=dev)
+        z = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+        canon = (q4.data_ptr(), s2.data_ptr(), z.data_ptr())
+    _check(qoq_pack_weights(W.data_ptr(), N, K, group, packed.data_ptr(), s1.data_ptr(), canon,
+                            0, _stream(dev)), "qoq_pack_weights")
+    return PackedWeight(packed, s1, N, K, group, q4, s2, z)
+
+
+def pack_canonical(q4: torch.Tensor, s2: torch.Tensor, z: torch.Tensor, s1: torch.Tensor,
+                   group: int = GROUP) -> PackedWeight:
+    """Pack caller-supplied canonical codes (QOQ_PACK_FROM_CANONICAL)."""
+    _need_gpu(q4, "q4", torch.uint8)
+    _need_gpu(s2, "s2", torch.int8)
+    _need_gpu(z, "z", torch.uint8)
+    _need_gpu(s1, "s1", torch.float16)
+    N, K = q4.shape
+    nbytes = qoq_packed_weight_bytes(N, K, group)
+    if nbytes == 0:
+        raise QoQError(2, "qoq_pack_weights")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=q4.device)
+    _check(qoq_pack_weights(None, N, K, group, packed.data_ptr(), None,
+                            (q4.data_ptr(), s2.data_ptr(), z.data_ptr()), PACK_FROM_CANONICAL,
+                            _stream(q4.device)), "qoq_pack_weights")
+    return PackedWeight(packed, s1, N, K, group, q4, s2, z)
+
+
+def quantize_act(x: torch.Tensor, out=None):
+    """Per-token INT8 quantization of x fp16 [M, K] -> (x8 int8, s_x fp32)."""
+    _need_gpu(x, "x", torch.float16)
+    M, K = x.shape
+    if out is None:
+        x8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        s_x = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        x8, s_x = out
+    _check(qoq_quantize_act(x.data_ptr(), M, K, x8.data_ptr(), s_x.data_ptr(),
+                            _stream(x.device)), "qoq_quantize_act")
+    return x8, s_x
+
+
+class Workspace:
+    """A zero-filled device buffer for split-K partial sums, grown on demand.
+
+    The library returns it to zero after every completed call, so one buffer
+    serves any number of sequential calls on one stream.
+    """
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if nbytes > self.buf.numel():
+            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8,
+                                   device=self.device)
+        return self.buf
+
+
+_WORKSPACES = {}
+
+
+def _default_workspace(device: torch.device) -> Workspace:
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    if key not in _WORKSPACES:
+        _WORKSPACES[key] = Workspace(torch.device("cuda", key[1]))
+    return _WORKSPACES[key]
+
+
+def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
+              y: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """y fp16 [M, N] = fp16(acc * s_x * s1); also returns acc int32 if asked."""
+    _need_gpu(x8, "x8", torch.int8)
+    _need_gpu(s_x, "s_x", torch.float32)
+    M, K = x8.shape
+    if K != w.K:
+        raise ValueError(f"x8 has K={K}, weights have K={w.K}")
+    dev = x8.device
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float16, device=dev)
+    acc = torch.empty((M, w.N), dtype=torch.int32, device=dev) if acc_debug else None
+    ws_bytes = qoq_gemm_workspace_bytes(M, w.N, K) if M > 0 else 0
+    ws_ptr = None
+    if ws_bytes:
+        ws = (workspace or _default_workspace(dev)).get(ws_bytes)
+        ws_ptr = ws.data_ptr()
+        ws_bytes = ws.numel()
+    _check(qoq_w4a8_gemm(x8.data_ptr(), s_x.data_ptr(), M, K, w.packed.data_ptr(),
+                         w.s1.data_ptr(), w.N, w.group, y.data_ptr(), _ptr(acc), ws_ptr,
+                         ws_bytes, _stream(dev)), "qoq_w4a8_gemm")
+    return (y, acc) if acc_debug else y

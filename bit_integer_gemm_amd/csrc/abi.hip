@@ -1,0 +1,114 @@
+// The C ABI of libqoq: host-side validation, then one or two kernel
+// launches on the caller's stream. Nothing here allocates, frees,
+// synchronizes or prints.
+#include "qoq.h"
+#include "qoq_internal.hpp"
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Largest K and N the 32-bit index arithmetic of the kernels supports.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+qoq_status check_weight_shape(int64_t N, int64_t K, int32_t group) {
+    if (group != qoq::kGroup) return QOQ_ERR_GROUP;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return QOQ_ERR_SHAPE;
+    if (N % qoq::kBlockCols != 0 || K % group != 0) return QOQ_ERR_SHAPE;
+    return QOQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
+    if (check_weight_shape(N, K, group) != QOQ_OK) return 0;
+    return size_t(qoq::packed_layout(N, K).total);
+}
+
+size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
+    return size_t(qoq::plan_gemm(M, N, K).ws_bytes);
+}
+
+qoq_status qoq_pack_weights(const float* W, int64_t N, int64_t K, int32_t group, void* packed,
+                            uint16_t* s1, const qoq_canonical* canon, uint32_t flags,
+                            void* stream) {
+    if (flags & ~QOQ_PACK_FROM_CANONICAL) return QOQ_ERR_FLAGS;
+    const bool from_canonical = (flags & QOQ_PACK_FROM_CANONICAL) != 0;
+    const qoq_status st = check_weight_shape(N, K, group);
+    if (st != QOQ_OK) return st;
+    if (packed == nullptr) return QOQ_ERR_NULL;
+    uint8_t* cq4 = nullptr;
+    int8_t* cs2 = nullptr;
+    uint8_t* cz = nullptr;
+    if (canon != nullptr) {
+        if (canon->q4 == nullptr || canon->s2 == nullptr || canon->z == nullptr)
+            return QOQ_ERR_NULL;
+        cq4 = canon->q4;
+        cs2 = canon->s2;
+        cz = canon->z;
+    }
+    if (from_canonical) {
+        if (canon == nullptr) return QOQ_ERR_NULL;
+    } else {
+        if (W == nullptr || s1 == nullptr) return QOQ_ERR_NULL;
+        if (misaligned(W)) return QOQ_ERR_ALIGN;
+    }
+    if (misaligned(packed)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_pack(W, N, K, static_cast<uint8_t*>(packed), s1, cq4, cs2, cz,
+                                          from_canonical, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x8, float* s_x,
+                            void* stream) {
+    if (M < 0 || K <= 0 || K % qoq::kGroup != 0 || M > kMaxDim || K > kMaxDim)
+        return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x == nullptr || x8 == nullptr || s_x == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(x) || misaligned(x8)) return QOQ_ERR_ALIGN;
+    const hipError_t e =
+        qoq::launch_quantize_act(x, M, K, x8, s_x, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
+                         const void* packed, const uint16_t* s1, int64_t N, int32_t group,
+                         uint16_t* y, int32_t* acc_debug, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    const qoq_status st = check_weight_shape(N, K, group);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x8 == nullptr || s_x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr)
+        return QOQ_ERR_NULL;
+    if (misaligned(x8) || misaligned(packed)) return QOQ_ERR_ALIGN;
+    const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);
+    if (plan.ws_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < size_t(plan.ws_bytes))
+            return QOQ_ERR_WORKSPACE;
+        if (misaligned(workspace)) return QOQ_ERR_ALIGN;
+    }
+    const hipError_t e = qoq::launch_gemm(plan, x8, s_x, M, K, static_cast<const uint8_t*>(packed),
+                                          s1, N, y, acc_debug, workspace,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+const char* qoq_status_string(int status) {
+    switch (status) {
+        case QOQ_OK: return "ok";
+        case QOQ_ERR_NULL: return "a required pointer is NULL";
+        case QOQ_ERR_SHAPE: return "invalid shape (sizes must be non-negative, N % 16 == 0, K % 128 == 0)";
+        case QOQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case QOQ_ERR_GROUP: return "unsupported group size (only 128)";
+        case QOQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case QOQ_ERR_HIP: return "HIP kernel launch failed";
+        case QOQ_ERR_FLAGS: return "unknown flag bits";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

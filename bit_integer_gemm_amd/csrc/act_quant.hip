@@ -1,0 +1,75 @@
+// Per-token symmetric INT8 quantization of the activations.
+//
+// The QServe abstract names 8-bit activations; the velog notes on QServe,
+// section "Background", pair per-channel weight scales with per-token
+// activation scales (that page's granularity labels are shifted by one item;
+// the per-token reading is the one the rest of the pages support).
+//
+// One workgroup per token. Pass 1 takes the row absmax (exact in any
+// reduction order: a max of exactly converted fp16 values); pass 2
+// re-reads the row (it is still in the L1/L2 caches) and writes the codes.
+// The row is read with 16-byte loads, 8 fp16 values per lane.
+#include "qoq_internal.hpp"
+
+#include <hip/hip_fp16.h>
+
+namespace qoq {
+namespace {
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half(uint16_t(bits16)));
+}
+
+__device__ __forceinline__ uint32_t quant_pair(uint32_t two_halves, float inv) {
+    const float a = rintf(h2f(two_halves & 0xffffu) * inv);
+    const float b = rintf(h2f(two_halves >> 16) * inv);
+    const int qa = int(fminf(fmaxf(a, -float(kActMax)), float(kActMax)));
+    const int qb = int(fminf(fmaxf(b, -float(kActMax)), float(kActMax)));
+    return (uint32_t(qa) & 0xffu) | ((uint32_t(qb) & 0xffu) << 8);
+}
+
+__global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t K, int8_t* __restrict__ x8,
+                                                        float* __restrict__ s_x) {
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = x + m * K;
+    int8_t* out = x8 + m * K;
+    // pass 1: absmax. For finite fp16, |x| ordering equals the ordering of the
+    // magnitude bits, so the max is taken on (bits & 0x7fff).
+    uint32_t mbits = 0;
+    for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mbits = max(mbits, w[i] & 0x7fffu);
+            mbits = max(mbits, (w[i] >> 16) & 0x7fffu);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), off, 64)));
+    __shared__ uint32_t part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mbits;
+    __syncthreads();
+    mbits = max(max(part[0], part[1]), max(part[2], part[3]));
+    const float a = h2f(mbits);
+    const float inv = a > 0.0f ? float(kActMax) / a : 0.0f;   // correctly rounded fp32
+    if (threadIdx.x == 0) s_x[m] = a > 0.0f ? a / float(kActMax) : 0.0f;
+    // pass 2: codes
+    for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+        uint2 o;
+        o.x = quant_pair(v.x, inv) | (quant_pair(v.y, inv) << 16);
+        o.y = quant_pair(v.z, inv) | (quant_pair(v.w, inv) << 16);
+        *reinterpret_cast<uint2*>(out + k) = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x8, float* s_x,
+                               hipStream_t stream) {
+    return launch_kernel(act_quant_kernel, dim3(unsigned(M)), dim3(256), 0, stream, x, K, x8,
+                         s_x);
+}
+
+}  // namespace qoq

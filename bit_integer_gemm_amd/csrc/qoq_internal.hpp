@@ -1,0 +1,108 @@
+// Internal declarations shared by the translation units of libqoq.
+//
+// Packed-weight layout, version 1 (what qoq_pack_weights writes and the
+// GEMM kernels read). N output channels, K inputs, groups of 128 inputs:
+//
+//   NB  = N / 16           column blocks of 16 output channels
+//   NG  = K / 128          groups per channel
+//   NG8 = ceil(NG / 8)     record chunks of 8 groups
+//
+//   nibbles  [NB][NG][64 lanes][16 bytes]       at byte 0
+//       The 1 KiB block (nb, g) is exactly the B operand of two
+//       v_mfma_i32_16x16x64_i8 steps for channels 16nb..16nb+15 and inputs
+//       128g..128g+127: lane l (channel 16nb + (l & 15), quarter h = l >> 4)
+//       owns 16 bytes; byte b holds the code of input 128g + 16h + b in its
+//       low nibble (first MFMA step, k in [0, 64) of the group) and of input
+//       128g + 64 + 16h + b in its high nibble (second step, k in [64, 128)).
+//       A wave fetches its fragments for one group with one 16-byte load per
+//       lane at base + 16 * lane, and `w & 0x0F0F0F0F` / `(w >> 4) &
+//       0x0F0F0F0F` put the codes of each 32-bit word directly into the byte
+//       order of the operand registers: no other address arithmetic and no
+//       byte permutes in the main loop (compute-aware reordering).
+//   records  [NB][NG8][16 channels][8 groups][2 bytes]   after the nibbles
+//       (s2, 128 - z*s2) as two uint8 per (channel, group); one 16-byte load
+//       gives a lane the records of 8 consecutive groups of its channel.
+//       Entries for groups >= NG are zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace qoq {
+
+// Launch through hipLaunchKernel so the status of this very launch is
+// returned (not whatever an unrelated earlier call left behind).
+template <typename... KArgs, typename Tuple, size_t... I>
+hipError_t launch_tuple(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                        hipStream_t stream, Tuple& args, std::index_sequence<I...>) {
+    void* argv[sizeof...(I) + 1] = {static_cast<void*>(&std::get<I>(args))..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem,
+                           stream);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> tup(std::forward<Args>(args)...);
+    return launch_tuple(kernel, grid, block, shmem, stream, tup,
+                        std::index_sequence_for<KArgs...>{});
+}
+
+constexpr int kGroup = 128;
+constexpr int kBlockCols = 16;
+constexpr int kBlockBytes = 1024;
+constexpr int kRecChunk = 8;
+constexpr int kRecChunkBytes = kBlockCols * kRecChunk * 2;  // 256
+constexpr int kProtect = 119;   // level-1 protective range
+constexpr int kActMax = 127;    // activation code bound
+
+struct PackedLayout {
+    int64_t nb, ng, ng8;
+    int64_t nib_bytes;
+    int64_t rec_offset;
+    int64_t rec_bytes;
+    int64_t total;
+};
+
+inline PackedLayout packed_layout(int64_t N, int64_t K) {
+    PackedLayout L;
+    L.nb = N / kBlockCols;
+    L.ng = K / kGroup;
+    L.ng8 = (L.ng + kRecChunk - 1) / kRecChunk;
+    L.nib_bytes = L.nb * L.ng * kBlockBytes;
+    L.rec_offset = L.nib_bytes;
+    L.rec_bytes = L.nb * L.ng8 * kRecChunkBytes;
+    L.total = L.nib_bytes + L.rec_bytes;
+    return L;
+}
+
+// Launch plan of the GEMM for one shape (host side, shared by the
+// workspace-size query and the launcher).
+struct GemmPlan {
+    int kind;           // 0: streaming tile family (all M)
+    int mt;             // 16-row MFMA tiles per wave
+    int cb;             // 16-column blocks per wave
+    int grid_x, grid_y, splits;
+    int groups_per_split;
+    int64_t ws_acc_bytes;   // int32 partial sums
+    int64_t ws_cnt_bytes;   // arrival counters
+    int64_t ws_bytes;       // total (0 when splits == 1)
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+// Launchers (enqueue only; return the launch status).
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed, uint16_t* s1,
+                       uint8_t* cq4, int8_t* cs2, uint8_t* cz, bool from_canonical,
+                       hipStream_t stream);
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x8, float* s_x,
+                               hipStream_t stream);
+hipError_t launch_gemm(const GemmPlan& plan, const int8_t* x8, const float* s_x, int64_t M,
+                       int64_t K, const uint8_t* packed, const uint16_t* s1, int64_t N,
+                       uint16_t* y, int32_t* acc_debug, void* workspace, hipStream_t stream);
+
+}  // namespace qoq

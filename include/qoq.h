@@ -1,0 +1,155 @@
+/*
+ * qoq.h -- C ABI of libqoq: the W4A8 GEMM of QoQ with progressive group
+ * quantization, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages: "QServe: W4A8KV4 Quantization and System
+ * Co-design for Efficient LLM Serving", sections "Methods / 1) Algorithm:
+ * QoQ" and "Methods / 2) System: QServe"; the QServe abstract; "Part5
+ * LLM部署技术", section 3 on QServe):
+ *
+ *   weights, offline   W[N,K] fp32 -> level 1: per-output-channel symmetric
+ *                      INT8 codes q8 in the protective range [-119, 119]
+ *                      with an FP16 scale s1[n];
+ *                      -> level 2: per group of 128 inputs of one channel,
+ *                      UINT4 codes q4 with an integer scale s2 in [1, 16]
+ *                      and a UINT4 zero z (dequantized w8 = q4*s2 - z*s2,
+ *                      always inside INT8);
+ *   activations        x[M,K] fp16 -> per-token symmetric INT8 x8 with an
+ *                      fp32 scale s_x[m];
+ *   GEMM               acc[m,n] = sum_k x8[m,k] * w8[n,k] in INT32 over the
+ *                      whole of K (no partial sum is ever scaled), then
+ *                      y[m,n] = fp16(acc * s_x[m] * s1[n]).
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are device pointers (hipMalloc'd or equivalent),
+ *     16-byte aligned, owned by the caller. The library never allocates,
+ *     frees or synchronizes; all work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and completes asynchronously.
+ *   - Shapes are checked on the host before anything is launched; on any
+ *     error nothing is launched and nothing is written.
+ *   - Integer results (codes, scales, accumulators) are deterministic and
+ *     independent of the launch configuration.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified
+ *     (but every memory access stays in bounds: indices depend on shapes
+ *     only).
+ *   - The library keeps no mutable global state; calls on different
+ *     streams are independent unless they share an output or a workspace.
+ */
+#ifndef QOQ_H
+#define QOQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qoq_status {
+    QOQ_OK = 0,
+    QOQ_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    QOQ_ERR_SHAPE = 2,     /* negative size, N % 16 != 0, K % group != 0 ...  */
+    QOQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                */
+    QOQ_ERR_GROUP = 4,     /* group size other than 128                       */
+    QOQ_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required         */
+    QOQ_ERR_HIP = 6,       /* a kernel launch failed (hipGetLastError)        */
+    QOQ_ERR_FLAGS = 7      /* unknown flag bits                               */
+} qoq_status;
+
+/* Group size of level 2 (inputs of one output channel per group). */
+#define QOQ_GROUP 128
+
+/* Version of the packed-weight layout produced by qoq_pack_weights. */
+#define QOQ_PACKED_LAYOUT_VERSION 1
+
+/* Flag for qoq_pack_weights: skip quantization and pack the caller's
+ * canonical (q4, s2, z) as they are. */
+#define QOQ_PACK_FROM_CANONICAL 0x1u
+
+/* Canonical level-2 output / input, all device pointers, row-major:
+ *   q4 [N*K]        one UINT4 code per byte (0..15), element (n, k) at n*K + k
+ *   s2 [N*K/128]    group scale, int8 in 1..16, group (n, g) at n*(K/128) + g
+ *   z  [N*K/128]    group zero, uint8 in 0..15
+ * When packing from canonical data the caller must keep every group inside
+ * the unpack's byte lanes: 0 <= q4*s2 + (128 - z*s2) <= 255 for all codes
+ * (true for anything level 2 produces, and for s2 = 1 with z in 0..15);
+ * otherwise the GEMM result is unspecified (still in bounds). */
+typedef struct qoq_canonical {
+    uint8_t* q4;
+    int8_t* s2;
+    uint8_t* z;
+} qoq_canonical;
+
+/* Bytes of the packed-weight buffer for an N x K weight (layout version 1):
+ * N*K/2 bytes of nibbles in MFMA operand order, then the per-group
+ * (s2, 128 - z*s2) byte pairs. Returns 0 for invalid shapes (N <= 0,
+ * K <= 0, N % 16 != 0, K % group != 0, group != 128). Host-only. */
+size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group);
+
+/* Progressive group quantization and compute-aware packing (offline).
+ * Pages: velog notes "Methods / 1) Algorithm: QoQ" (8-bit with per-channel
+ * FP16 scales, then 4-bit) and "Methods / 2) System: QServe" (protective
+ * range; compute-aware weight reordering).
+ *   W       [N,K] fp32, Linear layout (row n = output channel n). Ignored
+ *           (may be NULL) with QOQ_PACK_FROM_CANONICAL.
+ *   N, K    N % 16 == 0, K % group == 0, both > 0.
+ *   group   must be 128.
+ *   packed  out, qoq_packed_weight_bytes(N, K, group) bytes, opaque.
+ *   s1      out [N] fp16 bits (per-channel scale). Not written (may be
+ *           NULL) with QOQ_PACK_FROM_CANONICAL: the caller then owns s1.
+ *   canon   without the flag: NULL, or all three pointers non-NULL to also
+ *           receive the canonical codes; with the flag: required input.
+ *   flags   0 or QOQ_PACK_FROM_CANONICAL.
+ * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
+ * QOQ_ERR_FLAGS, QOQ_ERR_HIP. */
+qoq_status qoq_pack_weights(const float* W, int64_t N, int64_t K, int32_t group,
+                            void* packed, uint16_t* s1, const qoq_canonical* canon,
+                            uint32_t flags, void* stream);
+
+/* Per-token symmetric INT8 activation quantization (run time).
+ * Pages: QServe abstract (8-bit activations); velog notes "Background"
+ * (per-token activation scale next to per-channel weight scale).
+ *   x    [M,K] fp16 bits, row-major.   M >= 0, K > 0, K % 128 == 0.
+ *   x8   out [M,K] int8.               s_x  out [M] fp32.
+ * Row m: a = max|x[m,:]|; s_x = fp32(a/127); x8 = clamp(rne(x * fp32(127/a)),
+ * -127, 127); a zero row gives s_x = 0 and zero codes. M == 0 launches
+ * nothing. Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN, QOQ_ERR_HIP. */
+qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K,
+                            int8_t* x8, float* s_x, void* stream);
+
+/* Workspace bytes qoq_w4a8_gemm needs for this shape (0 if none). The
+ * workspace holds split-K INT32 partial sums and arrival counters. It must
+ * be zero-filled by the caller once, before its first use; every call that
+ * completes leaves it zero-filled again, so it can be reused by later calls
+ * on the same stream without clearing. Calls that overlap in time must not
+ * share a workspace. Host-only. */
+size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* W4A8 GEMM (run time, the hot path).
+ * Pages: velog notes "Methods / 1) Algorithm: QoQ" (every GEMM operation on
+ * INT8 matrix units), "Methods / 2) System: QServe" (register-level
+ * parallel INT4->INT8 dequantization, subtraction after multiplication) and
+ * "Background" (partial-sum dequantization in the main loop is the cost to
+ * avoid); "Part5 LLM部署技术" section 3 (no partial-sum dequantization).
+ *   x8, s_x      from qoq_quantize_act: [M,K] int8, [M] fp32.
+ *   M >= 0, K > 0, K % 128 == 0, N > 0, N % 16 == 0, group == 128.
+ *   packed, s1   from qoq_pack_weights for the same N, K.
+ *   y            out [M,N] fp16 bits, row-major: fp16(acc * s_x[m] * s1[n]).
+ *   acc_debug    NULL, or out [M,N] int32: the exact accumulators.
+ *   workspace    qoq_gemm_workspace_bytes(M, N, K) bytes (may be NULL when
+ *                that is 0), zero-filled before first use (see above).
+ * M == 0 launches nothing. Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE,
+ * QOQ_ERR_GROUP, QOQ_ERR_ALIGN, QOQ_ERR_WORKSPACE, QOQ_ERR_HIP. */
+qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
+                         const void* packed, const uint16_t* s1, int64_t N, int32_t group,
+                         uint16_t* y, int32_t* acc_debug,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* qoq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QOQ_H */

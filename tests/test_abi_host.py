@@ -1,0 +1,124 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry
+point its header declares, sizes buffers, and rejects invalid arguments with
+the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qoq.h")
+
+qoq = pytest.importorskip("bit_integer_gemm_amd")
+
+OK, NULL, SHAPE, ALIGN, GROUP, WORKSPACE, HIP, FLAGS = range(8)
+P = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qoq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = qoq.lib()
+    names = header_functions()
+    assert set(names) >= {"qoq_pack_weights", "qoq_quantize_act", "qoq_w4a8_gemm",
+                          "qoq_packed_weight_bytes", "qoq_gemm_workspace_bytes",
+                          "qoq_status_string"}
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for s in range(8):
+        assert qoq.qoq_status_string(s)
+    assert qoq.qoq_status_string(99) == "unknown status"
+
+
+def test_packed_weight_bytes():
+    # nibbles N*K/2 + records NB * ceil(NG/8) * 256
+    assert qoq.qoq_packed_weight_bytes(4096, 4096) == 4096 * 4096 // 2 + 256 * 4 * 256
+    assert qoq.qoq_packed_weight_bytes(16, 128) == 1024 + 256
+    assert qoq.qoq_packed_weight_bytes(16, 1152) == 9 * 1024 + 2 * 256
+    for bad in [(0, 128), (16, 0), (8, 128), (16, 64), (-16, 128), (16, 200)]:
+        assert qoq.qoq_packed_weight_bytes(*bad) == 0
+    assert qoq.qoq_packed_weight_bytes(16, 128, 64) == 0
+
+
+def test_workspace_bytes():
+    assert qoq.qoq_gemm_workspace_bytes(0, 4096, 4096) == 0
+    assert qoq.qoq_gemm_workspace_bytes(1, 10, 4096) == 0
+    for M in (1, 8, 32, 64):
+        ws = qoq.qoq_gemm_workspace_bytes(M, 4096, 4096)
+        if ws:
+            assert ws >= M * 4096 * 4 and ws % 256 == 0
+
+
+def test_pack_rejects_bad_arguments():
+    f = qoq.qoq_pack_weights
+    assert f(P, 4096, 4096, 64, P, P, None, 0, None) == GROUP
+    assert f(P, 4096, 4000, 128, P, P, None, 0, None) == SHAPE
+    assert f(P, 4090, 4096, 128, P, P, None, 0, None) == SHAPE
+    assert f(P, -16, 4096, 128, P, P, None, 0, None) == SHAPE
+    assert f(P, 16, 128, 128, P, P, None, 0x2, None) == FLAGS
+    assert f(None, 16, 128, 128, P, P, None, 0, None) == NULL
+    assert f(P, 16, 128, 128, None, P, None, 0, None) == NULL
+    assert f(P, 16, 128, 128, P, None, None, 0, None) == NULL
+    assert f(P + 4, 16, 128, 128, P, P, None, 0, None) == ALIGN
+    assert f(P, 16, 128, 128, P + 8, P, None, 0, None) == ALIGN
+    # canonical: input required with the flag, all three pointers or none
+    assert f(None, 16, 128, 128, P, None, None, 1, None) == NULL
+    assert f(None, 16, 128, 128, P, None, (P, 0, P), 1, None) == NULL
+    assert f(P, 16, 128, 128, P, P, (P, P, 0), 0, None) == NULL
+
+
+def test_quantize_act_rejects_bad_arguments():
+    f = qoq.qoq_quantize_act
+    assert f(P, -1, 128, P, P, None) == SHAPE
+    assert f(P, 4, 100, P, P, None) == SHAPE
+    assert f(P, 4, 0, P, P, None) == SHAPE
+    assert f(None, 4, 128, P, P, None) == NULL
+    assert f(P, 4, 128, None, P, None) == NULL
+    assert f(P, 4, 128, P, None, None) == NULL
+    assert f(P + 2, 4, 128, P, P, None) == ALIGN
+    assert f(P, 4, 128, P + 1, P, None) == ALIGN
+    assert f(None, 0, 128, None, None, None) == OK  # M == 0: nothing to do
+
+
+def test_gemm_rejects_bad_arguments():
+    f = qoq.qoq_w4a8_gemm
+    args = dict(x8=P, s_x=P, M=4, K=4096, packed=P, s1=P, N=4096, group=128, y=P,
+                acc_debug=None, workspace=None, workspace_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(group=64) == GROUP
+    assert call(K=4000) == SHAPE
+    assert call(N=4008) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(M=0) == OK
+    for name in ("x8", "s_x", "packed", "s1", "y"):
+        assert call(**{name: None}) == NULL, name
+    assert call(x8=P + 1) == ALIGN
+    assert call(packed=P + 8) == ALIGN
+    M, N, K = 1, 4096, 4096
+    need = qoq.qoq_gemm_workspace_bytes(M, N, K)
+    if need:
+        assert call(M=M, workspace=None, workspace_bytes=need) == WORKSPACE
+        assert call(M=M, workspace=P, workspace_bytes=need - 1) == WORKSPACE
+        assert call(M=M, workspace=P + 4, workspace_bytes=need) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        qoq.quantize_act(torch.zeros((2, 128), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qoq.pack_weights(torch.zeros((16, 128), dtype=torch.float32))

@@ -34,6 +34,7 @@ PACK_FROM_CANONICAL = 0x1
 QOQ_STATUS = {
     0: "QOQ_OK", 1: "QOQ_ERR_NULL", 2: "QOQ_ERR_SHAPE", 3: "QOQ_ERR_ALIGN",
     4: "QOQ_ERR_GROUP", 5: "QOQ_ERR_WORKSPACE", 6: "QOQ_ERR_HIP", 7: "QOQ_ERR_FLAGS",
+    8: "QOQ_ERR_CONFIG",
 }
 
 

@@ -29,7 +29,8 @@ size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
 
 size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
-    return size_t(qoq::plan_gemm(M, N, K).ws_bytes);
+    const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);
+    return plan.kind < 0 ? 0 : size_t(plan.ws_bytes);
 }
 
 qoq_status qoq_pack_weights(const float* W, int64_t N, int64_t K, int32_t group, void* packed,
@@ -84,8 +85,9 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
     if (M == 0) return QOQ_OK;
     if (x8 == nullptr || s_x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr)
         return QOQ_ERR_NULL;
-    if (misaligned(x8) || misaligned(packed)) return QOQ_ERR_ALIGN;
+    if (misaligned(x8) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
     const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);
+    if (plan.kind < 0) return QOQ_ERR_CONFIG;
     if (plan.ws_bytes > 0) {
         if (workspace == nullptr || workspace_bytes < size_t(plan.ws_bytes))
             return QOQ_ERR_WORKSPACE;
@@ -107,6 +109,7 @@ const char* qoq_status_string(int status) {
         case QOQ_ERR_WORKSPACE: return "workspace missing or too small";
         case QOQ_ERR_HIP: return "HIP kernel launch failed";
         case QOQ_ERR_FLAGS: return "unknown flag bits";
+        case QOQ_ERR_CONFIG: return "QOQ_GEMM_CONFIG names no compiled kernel configuration for this shape";
         default: return "unknown status";
     }
 }

@@ -19,10 +19,15 @@
 
 #include <hip/hip_fp16.h>
 
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
 namespace qoq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // Four UINT4 codes (one per byte) -> four INT8 weights, register-parallel.
@@ -39,16 +44,536 @@ __device__ __forceinline__ uint16_t epilogue_value(int32_t acc, float sx, float 
     return __half_as_ushort(__float2half_rn(v));
 }
 
-// Streaming tile family: a workgroup of 4 waves; wave w owns CB column
-// blocks (16 channels each) and MT row tiles (16 tokens each), over the
-// groups [g0, g1) of its split of K.
-template <int MT, int CB>
-__global__ void __launch_bounds__(256) gemm_stream_kernel(
+// One lane's 16 packed bytes (32 codes of one channel) -> the B operands of
+// the two MFMA steps of the group: low nibbles -> step 0, high -> step 1.
+// `rec` holds s2 in bits 0-7 and 128 - z*s2 in bits 8-15.
+__device__ __forceinline__ void dequant_block(const uint4 q, uint32_t rec, v4i& b0, v4i& b1) {
+    // byte permutes: s2 into both 16-bit halves, the bias into all four bytes
+    const uint32_t mul2 = __builtin_amdgcn_perm(0u, rec, 0x0c000c00u);
+    const uint32_t add2 = __builtin_amdgcn_perm(0u, rec, 0x01010101u);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b0[i] = dequant4(w[i] & 0x0F0F0F0Fu, mul2, add2);
+        b1[i] = dequant4((w[i] >> 4) & 0x0F0F0F0Fu, mul2, add2);
+    }
+}
+
+// Decode family (M <= 64): weight streaming.
+//
+// A workgroup owns CB column blocks (16 channels each) over the whole of K
+// and splits K between its KW waves in contiguous group ranges. Each wave
+// keeps PD groups of nibbles, records and activation fragments in flight
+// (register ring), so the HBM stream never waits on the MFMAs. The KW partial
+// INT32 accumulators are summed in LDS -- exact, so the result does not
+// depend on KW -- and the workgroup writes its outputs with the epilogue.
+// No partial sum ever leaves the workgroup: no global atomics, no fences.
+template <int MT, int CB, int KW, int PD>
+__global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
     const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_debug, int32_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ ws_cnt, int gps) {
+    int32_t* __restrict__ acc_debug) {
+    static_assert(KW * MT * CB <= 64, "LDS reduction buffer above 64 KiB");
+    __shared__ v4i red[KW * MT * CB * 64];
+    const int lane = threadIdx.x & 63;
+    // wave-uniform (scalar) so the group-range branches stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15;
+    const int h = lane >> 4;
+    const int ng = K >> 7;
+    const int nbt = N >> 4;
+    const int nb0 = blockIdx.x * CB;
+    const int gpw = (ng + KW - 1) / KW;
+    const int gb = min(ng, wave * gpw);
+    const int cnt = min(ng, gb + gpw) - gb;
+
+    const uint8_t* bptr[CB];
+    const uint8_t* rptr[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t nbc = min(nb0 + cb, nbt - 1);
+        bptr[cb] = nib + nbc * ng * kBlockBytes + lane * 16;
+        rptr[cb] = rec + (nbc * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    }
+    // Rows at or beyond M read a valid row instead (the last one): an MFMA
+    // row only feeds the same output row, and those rows are never stored.
+    // Unpredicated loads keep the prefetch ring free of per-lane branches.
+    const int8_t* aptr[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) aptr[mt] = x8 + int64_t(min(16 * mt + c, M - 1)) * K + 16 * h;
+
+    v4i acc[MT][CB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[mt][cb] = v4i{0, 0, 0, 0};
+
+    // Register ring of PD groups: group i of this wave lives in stage i % PD.
+    // A stage is consumed, then immediately refilled with the group PD ahead,
+    // so PD - 1 groups are always in flight while the MFMAs run.
+    uint4 qn[PD][CB];
+    uint32_t rs[PD][CB];
+    v4i av[PD][MT][2];
+
+    auto load = [&](int p, int g) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            qn[p][cb] = *reinterpret_cast<const uint4*>(bptr[cb] + int64_t(g) * kBlockBytes);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                av[p][mt][s] = *reinterpret_cast<const v4i*>(aptr[mt] + g * kGroup + 64 * s);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            rs[p][cb] = *reinterpret_cast<const uint16_t*>(
+                rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+    };
+
+    auto compute = [&](int p) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            v4i b0, b1;
+            dequant_block(qn[p][cb], rs[p][cb], b0, b1);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[p][mt][0], b0, acc[mt][cb], 0, 0, 0);
+                acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[p][mt][1], b1, acc[mt][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // The steady loop issues its loads unconditionally, so the wait before
+    // each stage only covers that stage (conditional loads would make the
+    // compiler drain the whole ring at the loop head). Group count per wave:
+    // cnt = q * PD + r.
+    const int nmain = cnt - cnt % PD;
+    if (nmain > 0) {
+#pragma unroll
+        for (int p = 0; p < PD; ++p) load(p, gb + p);
+        int i = 0;
+        for (; i + PD < nmain; i += PD) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                compute(p);
+                load(p, gb + i + p + PD);
+            }
+        }
+        // last full chunk: refill only with the remainder groups
+#pragma unroll
+        for (int p = 0; p < PD; ++p) {
+            compute(p);
+            if (nmain + p < cnt) load(p, gb + nmain + p);
+        }
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            if (nmain + p < cnt) compute(p);
+    } else {
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            if (p < cnt) load(p, gb + p);
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            if (p < cnt) compute(p);
+    }
+
+    // Sum the KW partial accumulators in LDS, then the epilogue. Output
+    // element (mt, r, h, cb, c) is token 16mt + 4h + r, channel
+    // 16(nb0 + cb) + c; consecutive threads take consecutive channels.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) red[((wave * MT + mt) * CB + cb) * 64 + lane] = acc[mt][cb];
+    __syncthreads();
+    const int* redi = reinterpret_cast<const int*>(red);
+    constexpr int E = MT * 16 * CB * 16;
+    for (int e = threadIdx.x; e < E; e += 64 * KW) {
+        const int cc = e & 15;
+        int t = e >> 4;
+        const int cbi = t % CB;
+        t /= CB;
+        const int hh = t & 3;
+        const int rr = (t >> 2) & 3;
+        const int mt = t >> 4;
+        const int m = 16 * mt + 4 * hh + rr;
+        const int nbi = nb0 + cbi;
+        if (m >= M || nbi >= nbt) continue;
+        const int l = cc + 16 * hh;
+        int32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) sum += redi[(((w * MT + mt) * CB + cbi) * 64 + l) * 4 + rr];
+        const int n = 16 * nbi + cc;
+        if (acc_debug) acc_debug[int64_t(m) * N + n] = sum;
+        y[int64_t(m) * N + n] = epilogue_value(sum, s_x[m], h2f(s1[n]));
+    }
+}
+
+// Shared-activation family (any M): a workgroup of NW waves covers
+// 16*MT tokens x 16*CB*NW channels over the whole of K. Wave w owns CB column
+// blocks and all MT row tiles, so every weight is dequantized exactly once
+// per workgroup and no B operand is shared. The INT8 activations of each
+// group (MT x 2 MFMA A fragments of 1 KiB) are staged in LDS once per
+// workgroup -- each wave fetches a share of the fragments into a register
+// ring P groups ahead and writes them to one of two LDS slots -- and all
+// waves read them from there. One barrier per group.
+template <int MT, int CB, int NW, int P>
+__global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
+    const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
+    const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
+    const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_debug) {
+    constexpr int AF = 2 * MT;                    // A fragments per group
+    constexpr int AFW = (AF + NW - 1) / NW;       // fragments fetched per wave
+    static_assert(P >= 2 && P % 2 == 0, "ring depth must be even");
+    __shared__ v4i As[2][AF][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15;
+    const int h = lane >> 4;
+    const int ng = K >> 7;
+    const int nbt = N >> 4;
+    const int nb0 = (blockIdx.x * NW + wave) * CB;
+    const int m0 = blockIdx.y * 16 * MT;
+
+    const uint8_t* bptr[CB];
+    const uint8_t* rptr[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t nbc = min(nb0 + cb, nbt - 1);
+        bptr[cb] = nib + nbc * ng * kBlockBytes + lane * 16;
+        rptr[cb] = rec + (nbc * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    }
+    // fragment f = wave + NW*j -> (row tile f >> 1, MFMA step f & 1); rows at
+    // or beyond M read the last row (never stored)
+    const int8_t* aptr[AFW];
+#pragma unroll
+    for (int j = 0; j < AFW; ++j) {
+        const int f = min(wave + NW * j, AF - 1);
+        const int row = min(m0 + 16 * (f >> 1) + c, M - 1);
+        aptr[j] = x8 + int64_t(row) * K + 64 * (f & 1) + 16 * h;
+    }
+    auto owns = [&](int j) { return wave + NW * j < AF; };
+
+    v4i acc[MT][CB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[mt][cb] = v4i{0, 0, 0, 0};
+
+    uint4 qn[P][CB];
+    uint32_t rs[P][CB];
+    v4i ar[P][AFW];
+
+    auto load_b = [&](int p, int g) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            qn[p][cb] = *reinterpret_cast<const uint4*>(bptr[cb] + int64_t(g) * kBlockBytes);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            rs[p][cb] = *reinterpret_cast<const uint16_t*>(
+                rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+    };
+    auto load_a = [&](int p, int g) {
+#pragma unroll
+        for (int j = 0; j < AFW; ++j)
+            ar[p][j] = *reinterpret_cast<const v4i*>(aptr[j] + int64_t(g) * kGroup);
+    };
+    auto stage_a = [&](int slot, int p) {
+#pragma unroll
+        for (int j = 0; j < AFW; ++j)
+            if (owns(j)) As[slot][wave + NW * j][lane] = ar[p][j];
+    };
+    auto compute = [&](int slot, int p) {
+        v4i b[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) dequant_block(qn[p][cb], rs[p][cb], b[cb][0], b[cb][1]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const v4i a0 = As[slot][2 * mt][lane];
+            const v4i a1 = As[slot][2 * mt + 1][lane];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b[cb][0], acc[mt][cb], 0, 0, 0);
+                acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b[cb][1], acc[mt][cb], 0, 0, 0);
+            }
+        }
+    };
+    // One group step. Every global load is unconditional -- groups past the
+    // last one are clamped to it (cache hits, never used) -- and only LDS
+    // staging and compute are guarded, so the compiler's waits cover exactly
+    // one stage of each ring and never drain them.
+    auto step = [&](int i, int p, bool full) {
+        const int pn = (p + 1) % P;
+        if (i + 1 < ng) stage_a((p + 1) & 1, pn);
+        load_a(pn, min(i + 1 + P, ng - 1));
+        if (full || i < ng) compute(p & 1, p);
+        load_b(p, min(i + P, ng - 1));
+        __syncthreads();
+    };
+
+    // Prologue: stage group 0, then issue the loads in the same order the
+    // steady state issues them (as if steps -P..-1 had run), so the loop is
+    // entered with the rings in their steady-state shape.
+    load_a(0, 0);
+    stage_a(0, 0);
+#pragma unroll
+    for (int j = -P; j < 0; ++j) {
+        load_a((j + 1 + P) % P, min(j + 1 + P, ng - 1));
+        load_b((j + P) % P, min(j + P, ng - 1));
+    }
+    __syncthreads();
+    int i0 = 0;
+    for (; i0 + P <= ng; i0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) step(i0 + p, p, true);
+    }
+    if (i0 < ng) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) step(i0 + p, p, false);
+    }
+
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        if (nb0 + cb >= nbt) continue;
+        const int n = 16 * (nb0 + cb) + c;
+        const float sw = h2f(s1[n]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * h + r;
+                if (m >= M) continue;
+                const int32_t v = acc[mt][cb][r];
+                if (acc_debug) acc_debug[int64_t(m) * N + n] = v;
+                y[int64_t(m) * N + n] = epilogue_value(v, s_x[m], sw);
+            }
+    }
+}
+
+// Tiles are assigned XCD-aware: the workgroups that land on one XCD (ids
+// congruent mod 8, the hardware's round-robin dispatch) take a contiguous run
+// of tiles in grouped order (8 tile rows at a time), so each XCD's L2 sees a
+// compact block of activation rows and weight columns.
+__device__ __forceinline__ void tile_of(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int T = tiles_m * tiles_n;
+    const int xcd = L & 7;
+    const int j = L >> 3;
+    const int per = T >> 3, extra = T & 7;
+    const int t = xcd * per + min(xcd, extra) + j;
+    constexpr int GM = 8;
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(GM, tiles_m - first_m);
+    const int in = t - group * GM * tiles_n;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// 32x32 tile family (large M), built on v_mfma_i32_32x32x32_i8 (the
+// 16x16x64 INT8 form issues at half the rate on gfx950). A workgroup of four
+// waves side by side along N computes a (32*MT) x (128*CB) tile over the
+// whole of K; wave w owns CB 32-column tiles and all MT 32-row tiles.
+//   * A (activations) of each group is staged once per workgroup in LDS, in
+//     32x32x32 fragment order: fragment (mt, s) holds, for lane l, the 16
+//     bytes x8[32mt + l%32][32s + 16(l/32) ...]; waves read them back with
+//     conflict-free 16-byte LDS reads. Two slots: group i+1 is staged while
+//     group i is consumed.
+//   * B (weights) comes straight from the packed buffer: for a 32-column
+//     tile, lane l (column l%32 of the tile, k-half q = l/32) loads the
+//     16-byte chunks of packed-block lanes c+16q and c+16(q+2) (c = l%16 in
+//     the block of its 16 columns); low nibbles of the two chunks are MFMA
+//     steps 0 and 1 of the group, high nibbles steps 2 and 3 -- the layout
+//     written for the 16x16x64 form serves this instruction unchanged.
+//   * Buffer loads: one per-lane VGPR offset per stream, everything uniform
+//     in SGPRs; out-of-range rows of A read as zero.
+//   * Register budget is kept under 256 (accumulators in AGPRs, shallow
+//     rings) so two workgroups share a CU: one's barrier waits, LDS latency
+//     and dequantization bursts are covered by the other's MFMAs.
+//   * Epilogue through LDS with 16-byte row-segment stores.
+template <int MT, int CB, int PB, int MINB>
+__global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
+    const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
+    const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
+    const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_debug) {
+    constexpr int AF = 4 * MT;                    // A fragments per group
+    constexpr int AFW = AF / 4;                   // fetched per wave (= MT)
+    static_assert(AF * 2 <= 64, "LDS slots above 64 KiB");
+    static_assert(PB >= 1 && PB <= 4, "weight ring depth");
+    __shared__ v4i As[2][AF][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31;
+    const int q = lane >> 5;
+    const int c = lane & 15;
+    const int ng = K >> 7;
+    const int nbt = N >> 4;
+    constexpr int BM = 32 * MT, BNB = 8 * CB;    // tile rows, tile 16-column blocks
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (nbt + BNB - 1) / BNB;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int nbw = tn * BNB + wave * 2 * CB;     // this wave's first 16-column block
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)x8, (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)nib, (short)0, nbt * ng * kBlockBytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)rec, (short)0, nbt * ng8 * (kBlockCols * kRecChunk * 2), 0x00020000);
+    const int a_lane = j * K + 16 * q;
+    int b_lane[CB], r_lane[CB];
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+        const int blk = min(nbw + 2 * t + (j >> 4), nbt - 1);
+        b_lane[t] = blk * ng * kBlockBytes + (c + 16 * q) * 16;
+        r_lane[t] = (blk * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    }
+
+    v16i acc[MT][CB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][t][r] = 0;
+
+    v4i ar[AFW];            // activation fragments of the next group to stage
+    uint4 qn[PB][CB][2];    // packed weights: group g in entry g % PB
+    uint32_t rs[PB][CB];
+
+    auto load_a = [&](int g) {
+        g = min(g, ng - 1);
+#pragma unroll
+        for (int u = 0; u < AFW; ++u) {
+            const int f = wave + 4 * u;
+            const int soff = (m0 + 32 * (f >> 2)) * K + g * kGroup + 32 * (f & 3);
+            ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane, soff, 0));
+        }
+    };
+    auto stage_a = [&](int slot) {
+#pragma unroll
+        for (int u = 0; u < AFW; ++u) As[slot][wave + 4 * u][lane] = ar[u];
+    };
+    auto load_b = [&](int p, int g) {
+        g = min(g, ng - 1);
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            qn[p][t][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rb, b_lane[t], g * kBlockBytes, 0));
+            qn[p][t][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rb, b_lane[t], g * kBlockBytes + 512, 0));
+        }
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+            rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(
+                rr, r_lane[t], (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2, 0);
+    };
+    // Step i: stage A(i+1), fetch A(i+2), dequantize B(i) and refill its
+    // entry with group i+PB, then the MFMAs of group i.
+    auto step = [&](int i, int u, bool full) {
+        if (i + 1 < ng) stage_a((u + 1) & 1);
+        load_a(i + 2);
+        v4i bq[CB][4];
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            dequant_block(qn[u % PB][t][0], rs[u % PB][t], bq[t][0], bq[t][2]);
+            dequant_block(qn[u % PB][t][1], rs[u % PB][t], bq[t][1], bq[t][3]);
+        }
+        load_b(u % PB, i + PB);
+        if (full || i < ng) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const v4i a = As[u & 1][4 * mt + st][lane];
+#pragma unroll
+                    for (int t = 0; t < CB; ++t)
+                        acc[mt][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq[t][st], acc[mt][t], 0, 0, 0);
+                }
+        }
+        __syncthreads();
+    };
+
+    // prologue, in steady-state issue order
+    load_a(0);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) load_b(p, p);
+    stage_a(0);
+    load_a(1);
+    __syncthreads();
+    constexpr int U = PB == 3 ? 6 : (PB == 1 ? 2 : PB);   // unroll: multiple of PB and of 2
+    int i0 = 0;
+    for (; i0 + U <= ng; i0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(i0 + u, u, true);
+    }
+    if (i0 < ng) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(i0 + u, u, false);
+    }
+
+    // Epilogue through LDS: per 32-row tile, each wave converts its 32 x 32CB
+    // block to fp16 into a staging area (reusing the A slots), then writes it
+    // out as 16-byte row segments. Lane (j, q), register r of tile (mt, t)
+    // holds row 32mt + 8(r/4) + 4q + r%4, column 32t + j of the wave's columns.
+    static_assert(4 * 32 * 32 * CB * 2 <= int(sizeof(As)), "staging does not fit the A slots");
+    __syncthreads();
+    uint16_t* stage = reinterpret_cast<uint16_t*>(&As[0][0][0]) + wave * (32 * 32 * CB);
+    const int n0w = 16 * nbw;
+    float sw[CB];
+#pragma unroll
+    for (int t = 0; t < CB; ++t) sw[t] = h2f(s1[min(n0w + 32 * t + j, N - 1)]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        float sxr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sxr[r] = s_x[min(m0 + 32 * mt + 8 * (r >> 2) + 4 * q + (r & 3), M - 1)];
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * q + (r & 3);
+                stage[row * (32 * CB) + 32 * t + j] = epilogue_value(acc[mt][t][r], sxr[r], sw[t]);
+            }
+        if (acc_debug) {
+#pragma unroll
+            for (int t = 0; t < CB; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + 32 * mt + 8 * (r >> 2) + 4 * q + (r & 3);
+                    const int n = n0w + 32 * t + j;
+                    if (m < M && n < N) acc_debug[int64_t(m) * N + n] = acc[mt][t][r];
+                }
+        }
+        __syncthreads();
+        // 32 rows x 4CB chunks of 16 bytes
+#pragma unroll
+        for (int u = 0; u < 2 * CB; ++u) {
+            const int kk = lane + 64 * u;
+            const int row = kk / (4 * CB);
+            const int ch = kk % (4 * CB);
+            const int m = m0 + 32 * mt + row;
+            const int n = n0w + 8 * ch;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (32 * CB) + 8 * ch);
+            if (m < M && n < N) *reinterpret_cast<uint4*>(y + int64_t(m) * N + n) = v;
+        }
+        __syncthreads();
+    }
+}
+
+// Generic family (any M): a workgroup of 4 waves, wave w owns CB column
+// blocks and MT row tiles over the whole of K. Kept for shapes no tuned
+// family covers.
+template <int MT, int CB>
+__global__ void __launch_bounds__(256) gemm_generic_kernel(
+    const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
+    const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
+    const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_debug) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15;
@@ -57,13 +582,10 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(
     const int nbt = N >> 4;
     const int nb_first = (blockIdx.x * 4 + wave) * CB;
     const int m0 = blockIdx.y * 16 * MT;
-    const int g0 = blockIdx.z * gps;
-    const int g1 = min(ng, g0 + gps);
 
     int nbc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) nbc[cb] = min(nb_first + cb, nbt - 1);
-
     const int8_t* arow[MT];
     bool aval[MT];
 #pragma unroll
@@ -72,14 +594,13 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(
         aval[mt] = r < M;
         arow[mt] = x8 + int64_t(aval[mt] ? r : 0) * K + 16 * h;
     }
-
     v4i acc[MT][CB];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[mt][cb] = v4i{0, 0, 0, 0};
 
-    for (int g = g0; g < g1; ++g) {
+    for (int g = 0; g < ng; ++g) {
         uint4 q[CB];
         uint32_t sb[CB];
 #pragma unroll
@@ -99,17 +620,8 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(
                                     : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const uint32_t s2 = sb[cb] & 0xffu;
-            const uint32_t bias = sb[cb] >> 8;
-            const uint32_t mul2 = s2 | (s2 << 16);
-            const uint32_t add2 = bias * 0x01010101u;
-            const uint32_t w[4] = {q[cb].x, q[cb].y, q[cb].z, q[cb].w};
             v4i b0, b1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b0[i] = dequant4(w[i] & 0x0F0F0F0Fu, mul2, add2);
-                b1[i] = dequant4((w[i] >> 4) & 0x0F0F0F0Fu, mul2, add2);
-            }
+            dequant_block(q[cb], sb[cb], b0, b1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], b0, acc[mt][cb], 0, 0, 0);
@@ -117,52 +629,6 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(
             }
         }
     }
-
-    // Output element of acc[mt][cb][r]: token m0 + 16mt + 4h + r, channel
-    // 16(nb_first + cb) + c (the 16x16 MFMA result layout).
-    if (gridDim.z == 1) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            if (nb_first + cb >= nbt) continue;
-            const int n = 16 * (nb_first + cb) + c;
-            const float sw = h2f(s1[n]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 16 * mt + 4 * h + r;
-                    if (m >= M) continue;
-                    const int32_t v = acc[mt][cb][r];
-                    if (acc_debug) acc_debug[int64_t(m) * N + n] = v;
-                    y[int64_t(m) * N + n] = epilogue_value(v, s_x[m], sw);
-                }
-        }
-        return;
-    }
-
-    // Split K: integer partial sums are combined with atomics (exact, order
-    // independent); the last workgroup of the tile to arrive runs the
-    // epilogue and returns the workspace to zero for the next call.
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        if (nb_first + cb >= nbt) continue;
-        const int n = 16 * (nb_first + cb) + c;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * h + r;
-                if (m < M) atomicAdd(ws_acc + int64_t(m) * N + n, acc[mt][cb][r]);
-            }
-    }
-    __threadfence();
-    __syncthreads();
-    __shared__ int is_last;
-    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    if (threadIdx.x == 0) is_last = atomicAdd(ws_cnt + tile, 1u) == gridDim.z - 1;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         if (nb_first + cb >= nbt) continue;
@@ -174,77 +640,214 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * h + r;
                 if (m >= M) continue;
-                int32_t* p = ws_acc + int64_t(m) * N + n;
-                const int32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int32_t v = acc[mt][cb][r];
                 if (acc_debug) acc_debug[int64_t(m) * N + n] = v;
                 y[int64_t(m) * N + n] = epilogue_value(v, s_x[m], sw);
-                *p = 0;
             }
     }
-    if (threadIdx.x == 0) ws_cnt[tile] = 0;
-}
-
-template <int MT, int CB>
-hipError_t launch_stream(const GemmPlan& p, const int8_t* x8, const float* s_x, int M, int K,
-                         const uint8_t* nib, const uint8_t* rec, int ng8, const uint16_t* s1,
-                         int N, uint16_t* y, int32_t* acc_debug, int32_t* ws_acc,
-                         uint32_t* ws_cnt, hipStream_t stream) {
-    return launch_kernel(gemm_stream_kernel<MT, CB>, dim3(p.grid_x, p.grid_y, p.splits),
-                         dim3(256), 0, stream, x8, s_x, M, K, nib, rec, ng8, s1, N, y, acc_debug,
-                         ws_acc, ws_cnt, p.groups_per_split);
 }
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+struct Args {
+    const int8_t* x8;
+    const float* s_x;
+    int M, K;
+    const uint8_t* nib;
+    const uint8_t* rec;
+    int ng8;
+    const uint16_t* s1;
+    int N;
+    uint16_t* y;
+    int32_t* acc_debug;
+};
+
+template <int MT, int CB, int KW, int PD>
+hipError_t launch_decode(const GemmPlan& p, const Args& a, hipStream_t stream) {
+    return launch_kernel(gemm_decode_kernel<MT, CB, KW, PD>, dim3(p.grid_x), dim3(64 * KW), 0,
+                         stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+                         a.acc_debug);
+}
+
+template <int MT, int CB, int NW, int P>
+hipError_t launch_lds(const GemmPlan& p, const Args& a, hipStream_t stream) {
+    return launch_kernel(gemm_lds_kernel<MT, CB, NW, P>, dim3(p.grid_x, p.grid_y), dim3(64 * NW),
+                         0, stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+                         a.acc_debug);
+}
+
+template <int MT, int CB, int PB, int MINB>
+hipError_t launch_tile32(const GemmPlan& p, const Args& a, hipStream_t stream) {
+    return launch_kernel(gemm_tile32_kernel<MT, CB, PB, MINB>, dim3(p.grid_x), dim3(256), 0, stream,
+                         a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y, a.acc_debug);
+}
+
+template <int MT, int CB>
+hipError_t launch_generic(const GemmPlan& p, const Args& a, hipStream_t stream) {
+    return launch_kernel(gemm_generic_kernel<MT, CB>, dim3(p.grid_x, p.grid_y), dim3(256), 0,
+                         stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+                         a.acc_debug);
+}
+
+// Every compiled decode configuration: (MT, CB, KW, PD).
+#define QOQ_DECODE_CONFIGS(X)                                                        \
+    X(1, 1, 16, 2) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 2, 4, 2) X(1, 4, 4, 2)            \
+    X(1, 4, 2, 2) X(1, 8, 2, 2) X(1, 1, 16, 4) X(1, 2, 8, 4) X(1, 4, 4, 4)            \
+    X(2, 1, 16, 2) X(2, 1, 8, 2) X(2, 2, 8, 2) X(2, 2, 4, 2) X(2, 4, 4, 2)            \
+    X(2, 4, 2, 2) X(2, 8, 2, 2) X(2, 2, 8, 4) X(2, 4, 4, 4)                           \
+    X(4, 1, 8, 2) X(4, 2, 8, 2) X(4, 2, 4, 2) X(4, 4, 4, 2) X(4, 4, 2, 2)             \
+    X(4, 4, 4, 4)
+
+// Every compiled shared-activation configuration: (MT, CB, NW, P).
+#define QOQ_LDS_CONFIGS(X)                                                           \
+    X(1, 1, 4, 2) X(1, 2, 4, 2) X(1, 1, 8, 2) X(1, 2, 8, 2) X(1, 4, 4, 2)             \
+    X(2, 1, 4, 2) X(2, 2, 4, 2) X(2, 1, 8, 2) X(2, 2, 8, 2) X(2, 4, 4, 2)             \
+    X(4, 1, 4, 2) X(4, 2, 4, 2) X(4, 1, 8, 2) X(4, 2, 8, 2) X(4, 4, 4, 2)             \
+    X(4, 1, 4, 4) X(4, 2, 4, 4) X(4, 1, 8, 4) X(4, 2, 8, 4)                           \
+    X(8, 2, 4, 2) X(8, 4, 4, 2) X(16, 2, 4, 2) X(16, 4, 4, 2) X(8, 2, 8, 2)
+
+bool lds_config_exists(int mt, int cb, int nw, int pp) {
+#define X(a, b, c, d) if (mt == a && cb == b && nw == c && pp == d) return true;
+    QOQ_LDS_CONFIGS(X)
+#undef X
+    return false;
+}
+
+// Every compiled 32x32 tile configuration: (MT, CB, PB, workgroups per CU).
+#define QOQ_TILE32_CONFIGS(X)                                                        \
+    X(4, 2, 2, 2) X(4, 2, 1, 2) X(4, 1, 2, 2) X(2, 2, 2, 2) X(2, 1, 2, 2) X(8, 1, 1, 2)  \
+    X(4, 2, 2, 1) X(8, 1, 2, 1) X(8, 2, 2, 1) X(2, 1, 2, 3) X(4, 1, 2, 3)
+
+bool tile32_config_exists(int mt, int cb, int pb, int minb) {
+#define X(a, b, c, d) if (mt == a && cb == b && pb == c && minb == d) return true;
+    QOQ_TILE32_CONFIGS(X)
+#undef X
+    return false;
+}
+
+bool decode_config_exists(int mt, int cb, int kw, int pd) {
+#define X(a, b, c, d) if (mt == a && cb == b && kw == c && pd == d) return true;
+    QOQ_DECODE_CONFIGS(X)
+#undef X
+    return false;
+}
+
 }  // namespace
 
+// Launch plan (defaults chosen from sweeps on MI355X over the workload
+// shapes; QOQ_GEMM_CONFIG="<family>,<params>" overrides it for A/B runs,
+// host-side only, and is ignored when it names no compiled configuration):
+//   M <= 64, N <= 8192:  decode family -- K split over the waves of a
+//                        workgroup, one or two column blocks per workgroup;
+//   M <= 64, N  > 8192:  shared-activation family -- activations staged in
+//                        LDS, waves side by side along N;
+//   M  > 64:             32x32 tile family, tile size picked so that at
+//                        least ~2 workgroups per CU exist.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p{};
-    p.kind = 0;
-    p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.cb = 2;
     const int64_t nbt = N / kBlockCols;
     const int64_t ng = K / kGroup;
-    p.grid_x = int((nbt + 4 * p.cb - 1) / (4 * p.cb));
-    p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
-    const int64_t base = int64_t(p.grid_x) * p.grid_y;
-    int64_t splits = 1;
-    if (base < 512) splits = std::min<int64_t>(ng, (1024 + base - 1) / base);
-    if (splits < 1) splits = 1;
-    const int64_t gps = (ng + splits - 1) / splits;
-    p.groups_per_split = int(gps);
-    p.splits = int((ng + gps - 1) / gps);
-    if (p.splits > 1) {
-        p.ws_acc_bytes = round_up(M * N * 4, 256);
-        p.ws_cnt_bytes = round_up(base * 4, 256);
-        p.ws_bytes = p.ws_acc_bytes + p.ws_cnt_bytes;
+    p.splits = 1;
+    p.groups_per_split = int(ng);
+    p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    // 32-bit buffer offsets: the fast families need N*K/2 and M*K below 2^31
+    const bool small_offsets = N * K / 2 < (int64_t(1) << 31) && M * K < (int64_t(1) << 31);
+    if (!small_offsets) {
+        p.kind = 0;
+        p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        p.cb = 2;
+    } else if (M <= 64 && nbt <= 512) {
+        p.kind = 1;
+        p.cb = 1;
+        p.kw = p.mt == 1 ? 16 : 8;
+        p.pd = p.mt == 1 ? 4 : 2;
+        while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
+        if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
+    } else if (M <= 64) {
+        p.kind = 2;
+        p.cb = nbt >= 2048 ? 2 : 1;
+        p.kw = 8;   // waves per workgroup
+        p.pd = 4;
+        if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) p.pd = 2;
+    } else {
+        p.kind = 4;
+        p.pd = 1;
+        p.pa = 2;   // workgroups per CU
+        const int64_t t42 = ((M + 127) / 128) * ((nbt + 15) / 16);
+        const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
+        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = N >= 16384 ? 1 : 2; }
+        else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
+        else { p.mt = 2; p.cb = 1; p.pd = 2; }
     }
+    if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
+        if (env[0] != '\0') {
+            int a = 0, b = 0, c = 0, d = 0;
+            char fam[16] = {0};
+            const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d", fam, &a, &b, &c, &d);
+            const std::string f(fam);
+            p.kind = -1;   // an override that names no compiled configuration is an error
+            if (f == "decode" && nf == 5 && M <= 16 * a && decode_config_exists(a, b, c, d)) {
+                p.kind = 1; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
+            } else if (f == "lds" && nf == 5 && lds_config_exists(a, b, c, d)) {
+                p.kind = 2; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
+            } else if (f == "tile32" && nf == 5 && small_offsets && tile32_config_exists(a, b, c, d)) {
+                p.kind = 4; p.mt = a; p.cb = b; p.pd = c; p.pa = d;
+            } else if (f == "generic" && nf >= 3 && (a == 1 || a == 2 || a == 4) && b == 2) {
+                p.kind = 0; p.mt = a; p.cb = b;
+            }
+            if (p.kind < 0) return p;
+        }
+    }
+    if (p.kind == 1) {
+        p.grid_x = int((nbt + p.cb - 1) / p.cb);
+        p.grid_y = 1;
+    } else if (p.kind == 4) {
+        const int64_t tm = (M + 32 * p.mt - 1) / (32 * p.mt);
+        const int64_t tn = (nbt + 8 * p.cb - 1) / (8 * p.cb);
+        p.grid_x = int(tm * tn);
+        p.grid_y = 1;
+    } else if (p.kind == 2) {
+        p.grid_x = int((nbt + p.cb * p.kw - 1) / (p.cb * p.kw));
+        p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
+    } else {
+        p.grid_x = int((nbt + 4 * p.cb - 1) / (4 * p.cb));
+        p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
+    }
+    p.ws_bytes = 0;
     return p;
 }
 
 hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, int64_t M, int64_t K,
                        const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
-                       int32_t* acc_debug, void* workspace, hipStream_t stream) {
+                       int32_t* acc_debug, void*, hipStream_t stream) {
     const PackedLayout L = packed_layout(N, K);
-    const uint8_t* nib = packed;
-    const uint8_t* rec = packed + L.rec_offset;
-    int32_t* ws_acc = nullptr;
-    uint32_t* ws_cnt = nullptr;
-    if (p.splits > 1) {
-        ws_acc = static_cast<int32_t*>(workspace);
-        ws_cnt = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + p.ws_acc_bytes);
+    const Args a{x8, s_x, int(M), int(K), packed, packed + L.rec_offset, int(L.ng8), s1, int(N),
+                 y, acc_debug};
+    if (p.kind == 1) {
+#define X(A, B, C, D) \
+    if (p.mt == A && p.cb == B && p.kw == C && p.pd == D) return launch_decode<A, B, C, D>(p, a, stream);
+        QOQ_DECODE_CONFIGS(X)
+#undef X
+        return hipErrorInvalidConfiguration;
     }
-    const int m = int(M), k = int(K), n = int(N), g8 = int(L.ng8);
+    if (p.kind == 4) {
+#define X(A, B, C, D) \
+    if (p.mt == A && p.cb == B && p.pd == C && p.pa == D) return launch_tile32<A, B, C, D>(p, a, stream);
+        QOQ_TILE32_CONFIGS(X)
+#undef X
+        return hipErrorInvalidConfiguration;
+    }
+    if (p.kind == 2) {
+#define X(A, B, C, D) \
+    if (p.mt == A && p.cb == B && p.kw == C && p.pd == D) return launch_lds<A, B, C, D>(p, a, stream);
+        QOQ_LDS_CONFIGS(X)
+#undef X
+        return hipErrorInvalidConfiguration;
+    }
     switch (p.mt) {
-        case 1:
-            return launch_stream<1, 2>(p, x8, s_x, m, k, nib, rec, g8, s1, n, y, acc_debug, ws_acc,
-                                       ws_cnt, stream);
-        case 2:
-            return launch_stream<2, 2>(p, x8, s_x, m, k, nib, rec, g8, s1, n, y, acc_debug, ws_acc,
-                                       ws_cnt, stream);
-        default:
-            return launch_stream<4, 2>(p, x8, s_x, m, k, nib, rec, g8, s1, n, y, acc_debug, ws_acc,
-                                       ws_cnt, stream);
+        case 1: return launch_generic<1, 2>(p, a, stream);
+        case 2: return launch_generic<2, 2>(p, a, stream);
+        default: return launch_generic<4, 2>(p, a, stream);
     }
 }
 

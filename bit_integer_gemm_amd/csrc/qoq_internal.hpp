@@ -83,9 +83,13 @@ inline PackedLayout packed_layout(int64_t N, int64_t K) {
 // Launch plan of the GEMM for one shape (host side, shared by the
 // workspace-size query and the launcher).
 struct GemmPlan {
-    int kind;           // 0: streaming tile family (all M)
+    int kind;           // 0: generic, 1: decode (K split over waves), 2: shared-activation,
+                        // 4: 32x32 tile (large M)
     int mt;             // 16-row MFMA tiles per wave
     int cb;             // 16-column blocks per wave
+    int kw;             // decode: waves splitting K; shared-activation: waves per workgroup
+    int pd;             // weight groups kept in flight per wave (register ring depth)
+    int pa;             // 32x32 tile: workgroups per CU the kernel is built for
     int grid_x, grid_y, splits;
     int groups_per_split;
     int64_t ws_acc_bytes;   // int32 partial sums

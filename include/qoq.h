@@ -22,7 +22,8 @@
  *
  * Conventions for every entry point:
  *   - All data pointers are device pointers (hipMalloc'd or equivalent),
- *     16-byte aligned, owned by the caller. The library never allocates,
+ *     owned by the caller; W, packed, x, x8, y and the workspace must be
+ *     16-byte aligned (checked), the others naturally aligned. The library never allocates,
  *     frees or synchronizes; all work is enqueued on `stream` (a
  *     hipStream_t; NULL = the null stream) and completes asynchronously.
  *   - Shapes are checked on the host before anything is launched; on any
@@ -53,7 +54,8 @@ typedef enum qoq_status {
     QOQ_ERR_GROUP = 4,     /* group size other than 128                       */
     QOQ_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required         */
     QOQ_ERR_HIP = 6,       /* a kernel launch failed (hipGetLastError)        */
-    QOQ_ERR_FLAGS = 7      /* unknown flag bits                               */
+    QOQ_ERR_FLAGS = 7,     /* unknown flag bits                               */
+    QOQ_ERR_CONFIG = 8     /* QOQ_GEMM_CONFIG names no compiled configuration */
 } qoq_status;
 
 /* Group size of level 2 (inputs of one output channel per group). */
@@ -138,8 +140,15 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   acc_debug    NULL, or out [M,N] int32: the exact accumulators.
  *   workspace    qoq_gemm_workspace_bytes(M, N, K) bytes (may be NULL when
  *                that is 0), zero-filled before first use (see above).
- * M == 0 launches nothing. Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE,
- * QOQ_ERR_GROUP, QOQ_ERR_ALIGN, QOQ_ERR_WORKSPACE, QOQ_ERR_HIP. */
+ * M == 0 launches nothing.
+ * Kernel choice: the library picks a kernel family and tile from (M, N, K).
+ * The environment variable QOQ_GEMM_CONFIG ("decode,MT,CB,KW,PD",
+ * "lds,MT,CB,NW,PD", "tile32,MT,CB,PB,WGPERCU" or "generic,MT,2") forces one
+ * compiled configuration for measurements; every configuration computes the
+ * same INT32 accumulators. A value naming no compiled configuration valid
+ * for the shape makes the call fail with QOQ_ERR_CONFIG (nothing launched).
+ * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
+ * QOQ_ERR_WORKSPACE, QOQ_ERR_CONFIG, QOQ_ERR_HIP. */
 qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
                          const void* packed, const uint16_t* s1, int64_t N, int32_t group,
                          uint16_t* y, int32_t* acc_debug,

@@ -122,3 +122,11 @@ def test_binding_refuses_cpu_tensors():
         qoq.quantize_act(torch.zeros((2, 128), dtype=torch.float16))
     with pytest.raises(ValueError):
         qoq.pack_weights(torch.zeros((16, 128), dtype=torch.float32))
+
+
+def test_unknown_kernel_override_is_rejected_before_launch(monkeypatch):
+    f = qoq.qoq_w4a8_gemm
+    for bad in ("tile32,99,1,1,1", "nonsense", "decode,9,9,9,9"):
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        assert f(P, P, 4, 4096, P, P, 4096, 128, P, None, None, 0, None) == 8
+        assert qoq.qoq_gemm_workspace_bytes(4, 4096, 4096) == 0

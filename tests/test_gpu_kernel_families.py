@@ -1,0 +1,101 @@
+"""Every compiled GEMM kernel configuration against the oracle.
+
+The library picks a kernel family and tile per shape; QOQ_GEMM_CONFIG forces
+one configuration (a name that is not compiled makes the call fail, so a
+silently ignored override cannot pass). Each configuration must give the
+oracle's INT32 accumulators bit-exactly on ragged shapes (odd group counts,
+column counts that fill no tile, token counts that fill no tile) and the fp16
+output within the relative tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+qoq = pytest.importorskip("bit_integer_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+DECODE = [(1, 1, 16, 2), (1, 1, 8, 2), (1, 2, 8, 2), (1, 2, 4, 2), (1, 4, 4, 2), (1, 4, 2, 2),
+          (1, 8, 2, 2), (1, 1, 16, 4), (1, 2, 8, 4), (1, 4, 4, 4), (2, 1, 16, 2), (2, 1, 8, 2),
+          (2, 2, 8, 2), (2, 2, 4, 2), (2, 4, 4, 2), (2, 4, 2, 2), (2, 8, 2, 2), (2, 2, 8, 4),
+          (2, 4, 4, 4), (4, 1, 8, 2), (4, 2, 8, 2), (4, 2, 4, 2), (4, 4, 4, 2), (4, 4, 2, 2),
+          (4, 4, 4, 4)]
+LDS = [(1, 1, 4, 2), (1, 2, 4, 2), (1, 1, 8, 2), (1, 2, 8, 2), (1, 4, 4, 2), (2, 1, 4, 2),
+       (2, 2, 4, 2), (2, 1, 8, 2), (2, 2, 8, 2), (2, 4, 4, 2), (4, 1, 4, 2), (4, 2, 4, 2),
+       (4, 1, 8, 2), (4, 2, 8, 2), (4, 4, 4, 2), (4, 1, 4, 4), (4, 2, 4, 4), (4, 1, 8, 4),
+       (4, 2, 8, 4), (8, 2, 4, 2), (8, 4, 4, 2), (16, 2, 4, 2), (16, 4, 4, 2), (8, 2, 8, 2)]
+TILE32 = [(4, 2, 2, 2), (4, 2, 1, 2), (4, 1, 2, 2), (2, 2, 2, 2), (2, 1, 2, 2), (8, 1, 1, 2),
+          (4, 2, 2, 1), (8, 1, 2, 1), (8, 2, 2, 1), (2, 1, 2, 3), (4, 1, 2, 3)]
+GENERIC = [(1, 2), (2, 2), (4, 2)]
+
+# (M, K, N): odd group counts, N not a multiple of any tile width
+SHAPES_SMALL_M = [(1, 640, 208), (13, 1152, 400), (37, 384, 48), (64, 2048, 528)]
+SHAPES_LARGE_M = [(100, 640, 208), (300, 1152, 528), (257, 256, 1040)]
+
+_cases = {}
+
+
+def _case(M, K, N):
+    key = (M, K, N)
+    if key not in _cases:
+        W, X, _ = wl.make_inputs(M, K, N, seed=M + 3 * K + 7 * N)
+        pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
+        x8, s_x = qoq.quantize_act(torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV))
+        ref = oracle.w4a8_linear(X, W)
+        _cases[key] = (pw, x8, s_x, ref)
+    return _cases[key]
+
+
+def _run(monkeypatch, cfg, M, K, N):
+    pw, x8, s_x, ref = _case(M, K, N)
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+    print(f"\n[gpu-case] {cfg} M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    got = acc.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, ref["acc"]), f"{cfg}: acc differs at {np.argwhere(got != ref['acc'])[:4]}"
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3, f"{cfg}: max rel err {err.max():.3e}"
+
+
+def _fmt(fam, cfg):
+    return fam + "," + ",".join(str(v) for v in cfg)
+
+
+@pytest.mark.parametrize("cfg", DECODE, ids=[_fmt("decode", c) for c in DECODE])
+def test_decode_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_SMALL_M:
+        if M <= 16 * cfg[0]:
+            _run(monkeypatch, _fmt("decode", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg", LDS, ids=[_fmt("lds", c) for c in LDS])
+def test_shared_activation_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_SMALL_M + SHAPES_LARGE_M[:1]:
+        _run(monkeypatch, _fmt("lds", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg", TILE32, ids=[_fmt("tile32", c) for c in TILE32])
+def test_tile32_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_LARGE_M + SHAPES_SMALL_M[1:2]:
+        _run(monkeypatch, _fmt("tile32", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg", GENERIC, ids=[_fmt("generic", c) for c in GENERIC])
+def test_generic_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_SMALL_M[:2] + SHAPES_LARGE_M[:1]:
+        _run(monkeypatch, _fmt("generic", cfg), M, K, N)
+
+
+def test_unknown_configuration_is_an_error(monkeypatch):
+    pw, x8, s_x, _ = _case(*SHAPES_SMALL_M[0])
+    for bad in ("tile32,99,1,1,1", "decode,1,3,3,3", "nonsense"):
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        with pytest.raises(qoq.QoQError) as e:
+            qoq.w4a8_gemm(x8, s_x, pw)
+        assert e.value.status == 8

@@ -15,8 +15,8 @@ Timing: each step is captured once per weight copy set into a HIP graph; K
 graph launches are timed with events on the capture stream. While the host
 enqueues, a spin kernel keeps the GPU busy, so launch overhead on the host
 never shows up as idle GPU time inside the timed region. Per-kernel
-durations of the GEMM (the dominant kernel) are taken the same way with an
-event pair around every launch.
+durations of the GEMM (the dominant kernel) are taken the same way: one event
+pair around many back-to-back launches, divided by their number.
 
 The other workloads (Llama-3-8B layers at M=256, the M=4096 prefill GEMM,
 Qwen1.5-72B layers at M=64 and M=1024) are timed GEMM by GEMM and listed
@@ -107,20 +107,24 @@ def event_pairs(torch, n):
 
 
 def per_launch_times(torch, blocker, fns, iters):
-    """Mean event-timed duration of each callable over `iters` round-robin
-    launches, enqueued behind the spin kernel."""
-    evs = [event_pairs(torch, iters) for _ in fns]
+    """Mean duration of each callable: one event pair around `iters`
+    back-to-back launches (enqueued behind the spin kernel), divided by
+    `iters`. Each entry of `fns` is a callable or a list of callables used
+    round robin (e.g. one per rotated weight copy)."""
+    out = []
+    for fn in fns:
+        seq = fn if isinstance(fn, (list, tuple)) else [fn]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def enqueue():
-        for it in range(iters):
-            for j, fn in enumerate(fns):
-                evs[j][it][0].record()
-                fn()
-                evs[j][it][1].record()
+        def enqueue():
+            a.record()
+            for it in range(iters):
+                seq[it % len(seq)]()
+            b.record()
 
-    # host cost estimate: ~40 us per launch with its two events
-    blocker.run(enqueue, 40e-6 * iters * len(fns))
-    return [float(np.mean([a.elapsed_time(b) for a, b in e])) * 1e-3 for e in evs]
+        blocker.run(enqueue, 30e-6 * iters)
+        out.append(a.elapsed_time(b) * 1e-3 / iters)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -269,20 +273,12 @@ def main():
     ops_step = sum(wl.algorithmic_ops(c["M"], K, N) for c in per_m)
     value_tops = ops_step / step_s / 1e12
 
-    # per-launch durations of the dominant kernel (GEMM) and of act quant
-    # (the GEMM launches rotate over the weight copies like the step does)
-    iters = max(64, n_phase)
-    evs = [event_pairs(torch, iters) for _ in range(n_m)]
-
-    def enqueue_gemms():
-        for it in range(iters):
-            for i in range(n_m):
-                evs[i][it][0].record()
-                phases[it % n_phase][i][1]()
-                evs[i][it][1].record()
-
-    blocker.run(enqueue_gemms, 40e-6 * iters * n_m)
-    gemm_t = [float(np.mean([a.elapsed_time(b) for a, b in evs[i]])) * 1e-3 for i in range(n_m)]
+    # per-launch durations of the dominant kernel (GEMM, rotating over the
+    # weight copies like the step does) and of the activation quantizer
+    iters = max(128, n_phase)
+    gemm_t = per_launch_times(torch, blocker,
+                              [[phases[j][i][1] for j in range(n_phase)] for i in range(n_m)],
+                              iters)
     act_t = per_launch_times(torch, blocker, [c["act"] for c in per_m], iters)
     gemm_bytes = [wl.algorithmic_bytes(c["M"], K, N) for c in per_m]
     achieved = sum(gemm_bytes) / sum(gemm_t) / 1e9
@@ -295,12 +291,14 @@ def main():
                                hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
                                mfma_frac=round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)))
 
-    # streaming-copy reference of the decode weight size, and of 1 GiB
+    # streaming-copy reference (a plain elementwise kernel: read N bytes, write
+    # N bytes) of the decode weight size and of 1 GiB; its counters calibrate
+    # the HBM-traffic counters of the GEMM
     copy_ref = {}
     for label, nbytes in (("decode_weights", pw.packed.numel()), ("1GiB", 1 << 30)):
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        t = per_launch_times(torch, blocker, [lambda: dst.copy_(src)], 20)[0]
+        t = per_launch_times(torch, blocker, [lambda: torch.bitwise_not(src, out=dst)], 20)[0]
         copy_ref[label] = {"bytes": nbytes, "us": round(t * 1e6, 3),
                            "gbs": round(2 * nbytes / t / 1e9, 1)}
         del src, dst
@@ -322,17 +320,7 @@ def main():
                 calls = [GemmCall(qoq, torch, xk8, sk, cp, pwk.s1, shp.N, yk, ws) for cp in ck]
                 for cl in calls[:3]:
                     cl()
-                it_n = max(args.shape_iters, len(calls))
-                ev = event_pairs(torch, it_n)
-
-                def enqueue():
-                    for it in range(it_n):
-                        ev[it][0].record()
-                        calls[it % len(calls)]()
-                        ev[it][1].record()
-
-                blocker.run(enqueue, 40e-6 * it_n)
-                t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+                t = per_launch_times(torch, blocker, [calls], max(args.shape_iters, len(calls)))[0]
                 ops = wl.algorithmic_ops(M, shp.K, shp.N)
                 b = wl.algorithmic_bytes(M, shp.K, shp.N)
                 t_floor = max(b / (HBM_PEAK_GBS * 1e9), ops / (INT8_PEAK_TOPS * 1e12))

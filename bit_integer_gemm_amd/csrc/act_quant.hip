@@ -6,9 +6,10 @@
 // the per-token reading is the one the rest of the pages support).
 //
 // One workgroup per token. Pass 1 takes the row absmax (exact in any
-// reduction order: a max of exactly converted fp16 values); pass 2
-// re-reads the row (it is still in the L1/L2 caches) and writes the codes.
-// The row is read with 16-byte loads, 8 fp16 values per lane.
+// reduction order: a max of exactly converted fp16 values); pass 2 writes the
+// codes from the values still held in registers (rows up to 8192 values) or
+// re-reads the row (longer rows; it is still in the caches). 16-byte loads,
+// 8 fp16 values per lane.
 #include "qoq_internal.hpp"
 
 #include <hip/hip_fp16.h>
@@ -28,6 +29,12 @@ __device__ __forceinline__ uint32_t quant_pair(uint32_t two_halves, float inv) {
     return (uint32_t(qa) & 0xffu) | ((uint32_t(qb) & 0xffu) << 8);
 }
 
+// Rows up to kRegK values are held in registers between the two passes (one
+// memory round trip); longer rows are re-read for the second pass.
+constexpr int kRegChunks = 4;                       // 16-byte chunks per thread
+constexpr int kRegK = 256 * 8 * kRegChunks;         // 8192 values
+
+template <bool kInRegs>
 __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ x,
                                                         int64_t K, int8_t* __restrict__ x8,
                                                         float* __restrict__ s_x) {
@@ -36,14 +43,28 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     int8_t* out = x8 + m * K;
     // pass 1: absmax. For finite fp16, |x| ordering equals the ordering of the
     // magnitude bits, so the max is taken on (bits & 0x7fff).
+    uint4 v[kRegChunks];
     uint32_t mbits = 0;
-    for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (kInRegs) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mbits = max(mbits, w[i] & 0x7fffu);
-            mbits = max(mbits, (w[i] >> 16) & 0x7fffu);
+        for (int u = 0; u < kRegChunks; ++u) {
+            const int64_t k = (int64_t(u) * 256 + threadIdx.x) * 8;
+            v[u] = k < K ? *reinterpret_cast<const uint4*>(row + k) : uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kRegChunks; ++u) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mbits = max(mbits, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+        }
+    } else {
+        for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8) {
+            const uint4 t = *reinterpret_cast<const uint4*>(row + k);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mbits = max(mbits, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
         }
     }
     for (int off = 32; off > 0; off >>= 1) mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), off, 64)));
@@ -55,12 +76,21 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     const float inv = a > 0.0f ? float(kActMax) / a : 0.0f;   // correctly rounded fp32
     if (threadIdx.x == 0) s_x[m] = a > 0.0f ? a / float(kActMax) : 0.0f;
     // pass 2: codes
-    for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+    auto emit = [&](const uint4 t, int64_t k) {
         uint2 o;
-        o.x = quant_pair(v.x, inv) | (quant_pair(v.y, inv) << 16);
-        o.y = quant_pair(v.z, inv) | (quant_pair(v.w, inv) << 16);
+        o.x = quant_pair(t.x, inv) | (quant_pair(t.y, inv) << 16);
+        o.y = quant_pair(t.z, inv) | (quant_pair(t.w, inv) << 16);
         *reinterpret_cast<uint2*>(out + k) = o;
+    };
+    if (kInRegs) {
+#pragma unroll
+        for (int u = 0; u < kRegChunks; ++u) {
+            const int64_t k = (int64_t(u) * 256 + threadIdx.x) * 8;
+            if (k < K) emit(v[u], k);
+        }
+    } else {
+        for (int64_t k = int64_t(threadIdx.x) * 8; k < K; k += 256 * 8)
+            emit(*reinterpret_cast<const uint4*>(row + k), k);
     }
 }
 
@@ -68,8 +98,11 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x8, float* s_x,
                                hipStream_t stream) {
-    return launch_kernel(act_quant_kernel, dim3(unsigned(M)), dim3(256), 0, stream, x, K, x8,
-                         s_x);
+    if (K <= kRegK)
+        return launch_kernel(act_quant_kernel<true>, dim3(unsigned(M)), dim3(256), 0, stream, x, K,
+                             x8, s_x);
+    return launch_kernel(act_quant_kernel<false>, dim3(unsigned(M)), dim3(256), 0, stream, x, K,
+                         x8, s_x);
 }
 
 }  // namespace qoq

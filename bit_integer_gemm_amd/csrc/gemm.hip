@@ -59,6 +59,12 @@ __device__ __forceinline__ void dequant_block(const uint4 q, uint32_t rec, v4i& 
     }
 }
 
+// Record of group (8j + u) from the 16-byte chunk of groups 8j..8j+7 (u static).
+__device__ __forceinline__ uint32_t record_of(const uint4 chunk, int u) {
+    const uint32_t w[4] = {chunk.x, chunk.y, chunk.z, chunk.w};
+    return (w[u >> 1] >> (16 * (u & 1))) & 0xffffu;
+}
+
 // Decode family (M <= 64): weight streaming.
 //
 // A workgroup owns CB column blocks (16 channels each) over the whole of K
@@ -262,17 +268,21 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
         for (int cb = 0; cb < CB; ++cb) acc[mt][cb] = v4i{0, 0, 0, 0};
 
     uint4 qn[P][CB];
-    uint32_t rs[P][CB];
     v4i ar[P][AFW];
+    // group records: one 16-byte load per lane brings 8 groups of its
+    // channel; the loop is unrolled by 8 so the group's slot is static
+    uint4 rc_cur[CB], rc_next[CB];
+    auto load_rec = [&](uint4 (&dst)[CB], int chunk) {
+        chunk = min(chunk, (ng - 1) >> 3);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            dst[cb] = *reinterpret_cast<const uint4*>(rptr[cb] + chunk * (kBlockCols * kRecChunk * 2));
+    };
 
     auto load_b = [&](int p, int g) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             qn[p][cb] = *reinterpret_cast<const uint4*>(bptr[cb] + int64_t(g) * kBlockBytes);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            rs[p][cb] = *reinterpret_cast<const uint16_t*>(
-                rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
     };
     auto load_a = [&](int p, int g) {
 #pragma unroll
@@ -284,10 +294,11 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
         for (int j = 0; j < AFW; ++j)
             if (owns(j)) As[slot][wave + NW * j][lane] = ar[p][j];
     };
-    auto compute = [&](int slot, int p) {
+    auto compute = [&](int slot, int p, int u) {
         v4i b[CB][2];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) dequant_block(qn[p][cb], rs[p][cb], b[cb][0], b[cb][1]);
+        for (int cb = 0; cb < CB; ++cb)
+            dequant_block(qn[p][cb], record_of(rc_cur[cb], u), b[cb][0], b[cb][1]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const v4i a0 = As[slot][2 * mt][lane];
@@ -303,18 +314,26 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
     // last one are clamped to it (cache hits, never used) -- and only LDS
     // staging and compute are guarded, so the compiler's waits cover exactly
     // one stage of each ring and never drain them.
-    auto step = [&](int i, int p, bool full) {
+    auto step = [&](int i, int u, bool full) {
+        const int p = u % P;
         const int pn = (p + 1) % P;
         if (i + 1 < ng) stage_a((p + 1) & 1, pn);
         load_a(pn, min(i + 1 + P, ng - 1));
-        if (full || i < ng) compute(p & 1, p);
+        if (full || i < ng) compute(p & 1, p, u);
         load_b(p, min(i + P, ng - 1));
+        if (u == 7) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) rc_cur[cb] = rc_next[cb];
+            load_rec(rc_next, ((i + 1) >> 3) + 1);
+        }
         __syncthreads();
     };
 
     // Prologue: stage group 0, then issue the loads in the same order the
     // steady state issues them (as if steps -P..-1 had run), so the loop is
     // entered with the rings in their steady-state shape.
+    load_rec(rc_cur, 0);
+    load_rec(rc_next, 1);
     load_a(0, 0);
     stage_a(0, 0);
 #pragma unroll
@@ -323,14 +342,15 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
         load_b((j + P) % P, min(j + P, ng - 1));
     }
     __syncthreads();
+    static_assert(8 % P == 0, "ring depth must divide the record chunk");
     int i0 = 0;
-    for (; i0 + P <= ng; i0 += P) {
+    for (; i0 + 8 <= ng; i0 += 8) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) step(i0 + p, p, true);
+        for (int u = 0; u < 8; ++u) step(i0 + u, u, true);
     }
     if (i0 < ng) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) step(i0 + p, p, false);
+        for (int u = 0; u < 8; ++u) step(i0 + u, u, false);
     }
 
 #pragma unroll
@@ -442,7 +462,16 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
 
     v4i ar[AFW];            // activation fragments of the next group to stage
     uint4 qn[PB][CB][2];    // packed weights: group g in entry g % PB
-    uint32_t rs[PB][CB];
+    // group records: one 16-byte load per lane brings 8 groups of its
+    // channel; the loop is unrolled by 8 so the group's slot is static
+    uint4 rc_cur[CB], rc_next[CB];
+    auto load_rec = [&](uint4 (&dst)[CB], int chunk) {
+        chunk = min(chunk, (ng - 1) >> 3);
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+            dst[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rr, r_lane[t], chunk * (kBlockCols * kRecChunk * 2), 0));
+    };
 
     auto load_a = [&](int g) {
         g = min(g, ng - 1);
@@ -466,10 +495,6 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
             qn[p][t][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rb, b_lane[t], g * kBlockBytes + 512, 0));
         }
-#pragma unroll
-        for (int t = 0; t < CB; ++t)
-            rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(
-                rr, r_lane[t], (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2, 0);
     };
     // Step i: stage A(i+1), fetch A(i+2), dequantize B(i) and refill its
     // entry with group i+PB, then the MFMAs of group i.
@@ -479,10 +504,16 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
         v4i bq[CB][4];
 #pragma unroll
         for (int t = 0; t < CB; ++t) {
-            dequant_block(qn[u % PB][t][0], rs[u % PB][t], bq[t][0], bq[t][2]);
-            dequant_block(qn[u % PB][t][1], rs[u % PB][t], bq[t][1], bq[t][3]);
+            const uint32_t rec_u = record_of(rc_cur[t], u);
+            dequant_block(qn[u % PB][t][0], rec_u, bq[t][0], bq[t][2]);
+            dequant_block(qn[u % PB][t][1], rec_u, bq[t][1], bq[t][3]);
         }
         load_b(u % PB, i + PB);
+        if (u == 7) {
+#pragma unroll
+            for (int t = 0; t < CB; ++t) rc_cur[t] = rc_next[t];
+            load_rec(rc_next, ((i + 1) >> 3) + 1);
+        }
         if (full || i < ng) {
 #pragma unroll
             for (int st = 0; st < 4; ++st)
@@ -498,13 +529,16 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
     };
 
     // prologue, in steady-state issue order
+    load_rec(rc_cur, 0);
+    load_rec(rc_next, 1);
     load_a(0);
 #pragma unroll
     for (int p = 0; p < PB; ++p) load_b(p, p);
     stage_a(0);
     load_a(1);
     __syncthreads();
-    constexpr int U = PB == 3 ? 6 : (PB == 1 ? 2 : PB);   // unroll: multiple of PB and of 2
+    constexpr int U = 8;    // unroll: one record chunk; a multiple of PB and of 2
+    static_assert(U % PB == 0, "ring depth must divide the record chunk");
     int i0 = 0;
     for (; i0 + U <= ng; i0 += U) {
 #pragma unroll
@@ -704,7 +738,10 @@ hipError_t launch_generic(const GemmPlan& p, const Args& a, hipStream_t stream) 
     X(2, 1, 4, 2) X(2, 2, 4, 2) X(2, 1, 8, 2) X(2, 2, 8, 2) X(2, 4, 4, 2)             \
     X(4, 1, 4, 2) X(4, 2, 4, 2) X(4, 1, 8, 2) X(4, 2, 8, 2) X(4, 4, 4, 2)             \
     X(4, 1, 4, 4) X(4, 2, 4, 4) X(4, 1, 8, 4) X(4, 2, 8, 4)                           \
-    X(8, 2, 4, 2) X(8, 4, 4, 2) X(16, 2, 4, 2) X(16, 4, 4, 2) X(8, 2, 8, 2)
+    X(8, 2, 4, 2) X(8, 4, 4, 2) X(16, 2, 4, 2) X(16, 4, 4, 2) X(8, 2, 8, 2)             \
+    X(4, 1, 6, 4) X(4, 2, 6, 4) X(4, 1, 12, 4) X(4, 1, 12, 2) X(4, 1, 16, 2)            \
+    X(1, 1, 6, 4) X(1, 1, 12, 4) X(2, 1, 6, 4) X(2, 1, 12, 4) X(4, 1, 12, 8)             \
+    X(4, 1, 8, 8) X(4, 1, 6, 8) X(4, 2, 6, 8) X(4, 1, 4, 8)
 
 bool lds_config_exists(int mt, int cb, int nw, int pp) {
 #define X(a, b, c, d) if (mt == a && cb == b && nw == c && pp == d) return true;
@@ -758,17 +795,27 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.cb = 2;
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
-        p.cb = 1;
+        p.cb = nbt >= 512 ? 2 : 1;
         p.kw = p.mt == 1 ? 16 : 8;
         p.pd = p.mt == 1 ? 4 : 2;
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
     } else if (M <= 64) {
+        // waves per workgroup chosen so the workgroup count is a multiple of
+        // the 256 CUs (no tail round), preferring more workgroups
         p.kind = 2;
-        p.cb = nbt >= 2048 ? 2 : 1;
-        p.kw = 8;   // waves per workgroup
+        p.cb = 1;
         p.pd = 4;
-        if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) p.pd = 2;
+        p.kw = 8;
+        int64_t best = -1;
+        for (int nw : {4, 6, 8, 12}) {
+            if (!lds_config_exists(p.mt, 1, nw, 4)) continue;
+            const int64_t wgs = (nbt + nw - 1) / nw;
+            const int64_t rounds = (wgs + 255) / 256;
+            const int64_t score = wgs * 1000 / (rounds * 256) * 4 + nw;   // fill, then waves
+            if (wgs >= 256 && score > best) { best = score; p.kw = nw; }
+        }
+        if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
     } else {
         p.kind = 4;
         p.pd = 1;

@@ -22,6 +22,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 namespace qoq {
 namespace {
@@ -117,12 +118,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
 
     // Register ring of PD groups: group i of this wave lives in stage i % PD.
     // A stage is consumed, then immediately refilled with the group PD ahead,
-    // so PD - 1 groups are always in flight while the MFMAs run.
+    // so PD - 1 groups are always in flight while the MFMAs run. Loads are
+    // unconditional (past the range they repeat the last group: cache hits,
+    // never used) so the compiler's waits cover one stage at a time.
+    // Group records: when every wave's range starts on a multiple of 8, one
+    // 16-byte load per 8 groups (static slot in a loop unrolled by 8);
+    // otherwise one 2-byte load per group.
+    static_assert(8 % PD == 0, "ring depth must divide the record chunk");
     uint4 qn[PD][CB];
     uint32_t rs[PD][CB];
     v4i av[PD][MT][2];
+    uint4 rc_cur[CB], rc_next[CB];
+    const bool aligned = (gpw & 7) == 0;
 
-    auto load = [&](int p, int g) {
+    auto load = [&](int p, int g, bool per_group_rec) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             qn[p][cb] = *reinterpret_cast<const uint4*>(bptr[cb] + int64_t(g) * kBlockBytes);
@@ -131,17 +140,24 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 av[p][mt][s] = *reinterpret_cast<const v4i*>(aptr[mt] + g * kGroup + 64 * s);
+        if (per_group_rec) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                rs[p][cb] = *reinterpret_cast<const uint16_t*>(
+                    rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+        }
+    };
+    auto load_rec = [&](uint4 (&dst)[CB], int chunk) {
+        chunk = min(chunk, (ng - 1) >> 3);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-            rs[p][cb] = *reinterpret_cast<const uint16_t*>(
-                rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+            dst[cb] = *reinterpret_cast<const uint4*>(rptr[cb] + chunk * (kBlockCols * kRecChunk * 2));
     };
-
-    auto compute = [&](int p) {
+    auto compute = [&](int p, uint32_t const (&rec)[CB]) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             v4i b0, b1;
-            dequant_block(qn[p][cb], rs[p][cb], b0, b1);
+            dequant_block(qn[p][cb], rec[cb], b0, b1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 acc[mt][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[p][mt][0], b0, acc[mt][cb], 0, 0, 0);
@@ -149,39 +165,49 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
             }
         }
     };
-
-    // The steady loop issues its loads unconditionally, so the wait before
-    // each stage only covers that stage (conditional loads would make the
-    // compiler drain the whole ring at the loop head). Group count per wave:
-    // cnt = q * PD + r.
-    const int nmain = cnt - cnt % PD;
-    if (nmain > 0) {
+    auto run = [&](auto chunked) {
+        constexpr bool kChunked = decltype(chunked)::value;
+        auto step = [&](int i, int u, bool full) {
+            const int p = u % PD;
+            if (full || i < cnt) {
+                uint32_t rec[CB];
 #pragma unroll
-        for (int p = 0; p < PD; ++p) load(p, gb + p);
-        int i = 0;
-        for (; i + PD < nmain; i += PD) {
-#pragma unroll
-            for (int p = 0; p < PD; ++p) {
-                compute(p);
-                load(p, gb + i + p + PD);
+                for (int cb = 0; cb < CB; ++cb) rec[cb] = kChunked ? record_of(rc_cur[cb], u) : rs[p][cb];
+                compute(p, rec);
             }
+            // in the final (guarded) block only the loads still needed are issued
+            if (full || i + PD < cnt) load(p, gb + min(i + PD, cnt - 1), !kChunked);
+            if (kChunked && u == 7) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) rc_cur[cb] = rc_next[cb];
+                load_rec(rc_next, ((gb + i + 1) >> 3) + 1);
+            }
+        };
+        if (kChunked) {
+            load_rec(rc_cur, gb >> 3);
+            load_rec(rc_next, (gb >> 3) + 1);
         }
-        // last full chunk: refill only with the remainder groups
+        if (cnt >= PD) {
 #pragma unroll
-        for (int p = 0; p < PD; ++p) {
-            compute(p);
-            if (nmain + p < cnt) load(p, gb + nmain + p);
+            for (int p = 0; p < PD; ++p) load(p, gb + p, !kChunked);
+        } else {
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+                if (p < cnt) load(p, gb + p, !kChunked);
         }
+        int i0 = 0;
+        for (; i0 + 8 <= cnt; i0 += 8) {
 #pragma unroll
-        for (int p = 0; p < PD; ++p)
-            if (nmain + p < cnt) compute(p);
-    } else {
+            for (int u = 0; u < 8; ++u) step(i0 + u, u, true);
+        }
+        if (i0 < cnt) {
 #pragma unroll
-        for (int p = 0; p < PD; ++p)
-            if (p < cnt) load(p, gb + p);
-#pragma unroll
-        for (int p = 0; p < PD; ++p)
-            if (p < cnt) compute(p);
+            for (int u = 0; u < 8; ++u) step(i0 + u, u, false);
+        }
+    };
+    if (cnt > 0) {
+        if (aligned) run(std::true_type{});
+        else run(std::false_type{});
     }
 
     // Sum the KW partial accumulators in LDS, then the epilogue. Output
@@ -795,34 +821,24 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.cb = 2;
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
-        p.cb = nbt >= 512 ? 2 : 1;
-        p.kw = p.mt == 1 ? 16 : 8;
-        p.pd = p.mt == 1 ? 4 : 2;
+        if (p.mt == 1) { p.cb = 1; p.kw = 16; p.pd = 4; }
+        else if (p.mt == 2) { p.cb = 1; p.kw = 8; p.pd = 2; }
+        else if (nbt >= 512) { p.cb = 2; p.kw = 4; p.pd = 2; }
+        else { p.cb = 1; p.kw = 8; p.pd = 2; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
-        if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
+        if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
     } else if (M <= 64) {
-        // waves per workgroup chosen so the workgroup count is a multiple of
-        // the 256 CUs (no tail round), preferring more workgroups
         p.kind = 2;
         p.cb = 1;
-        p.pd = 4;
-        p.kw = 8;
-        int64_t best = -1;
-        for (int nw : {4, 6, 8, 12}) {
-            if (!lds_config_exists(p.mt, 1, nw, 4)) continue;
-            const int64_t wgs = (nbt + nw - 1) / nw;
-            const int64_t rounds = (wgs + 255) / 256;
-            const int64_t score = wgs * 1000 / (rounds * 256) * 4 + nw;   // fill, then waves
-            if (wgs >= 256 && score > best) { best = score; p.kw = nw; }
-        }
+        if (nbt >= 2048) { p.kw = 12; p.pd = 2; }   // waves per workgroup, ring depth
+        else { p.kw = 8; p.pd = 4; }
         if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
     } else {
         p.kind = 4;
-        p.pd = 1;
         p.pa = 2;   // workgroups per CU
         const int64_t t42 = ((M + 127) / 128) * ((nbt + 15) / 16);
         const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
-        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = N >= 16384 ? 1 : 2; }
+        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 1; }
         else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
         else { p.mt = 2; p.cb = 1; p.pd = 2; }
     }

@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -235,27 +236,31 @@ def main():
             act()
             gemm()
 
-    # capture one graph per phase (on torch's capture stream)
+    # capture the step into HIP graphs of G consecutive steps (G divides both
+    # the step count and the number of weight-copy phases), on torch's
+    # capture stream; replaying K/G graphs times exactly K steps
+    G = math.gcd(args.steps, n_phase)
     for j in range(n_phase):
         eager_step(j)
     torch.cuda.synchronize()
     graphs = []
-    for j in range(n_phase):
+    for g0 in range(0, n_phase, G):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            eager_step(j)
+            for j in range(g0, g0 + G):
+                eager_step(j)
         graphs.append(g)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        graphs[i % n_phase].replay()
+    for i in range(-(-args.warmup // G)):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed_graph_steps():
         start.record()
-        for i in range(args.steps):
-            graphs[i % n_phase].replay()
+        for i in range(args.steps // G):
+            graphs[i % len(graphs)].replay()
         end.record()
 
     _, host_s, covered = blocker.run(timed_graph_steps, 30e-6 * args.steps)
@@ -361,6 +366,7 @@ def main():
                                "algorithmic bytes / mean event-timed launch duration"},
         "cpu_baseline": cpu,
         "step_eager_ms": round(eager_step_s * 1e3, 6),
+        "steps_per_graph": G,
         "host_enqueue_covered": covered,
         "pack": {"N": N, "K": K, "us": round(pack_t * 1e6, 1),
                  "weights_per_s": round(N * K / pack_t, 1),

@@ -799,7 +799,8 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 
 // Launch plan (defaults chosen from sweeps on MI355X over the workload
 // shapes; QOQ_GEMM_CONFIG="<family>,<params>" overrides it for A/B runs,
-// host-side only, and is ignored when it names no compiled configuration):
+// host-side only; a value naming no compiled configuration makes the call
+// fail before anything is launched):
 //   M <= 64, N <= 8192:  decode family -- K split over the waves of a
 //                        workgroup, one or two column blocks per workgroup;
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in

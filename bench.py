@@ -143,7 +143,7 @@ class GemmCall:
     """A prepared qoq_w4a8_gemm call (pointers resolved once)."""
 
     def __init__(self, qoq, torch, x8, s_x, packed, s1, N, y, ws):
-        M, K = x8.shape
+        M, K = s_x.shape[0], x8.shape[1] * 16
         self.f = qoq.lib().qoq_w4a8_gemm
         wsb = qoq.qoq_gemm_workspace_bytes(M, N, K)
         wsp = None
@@ -216,7 +216,7 @@ def main():
     for M in dw.Ms:
         _, Xm, _ = wl.make_case(dw, shape, M)
         c = dict(M=M, x=to_half_device(torch, Xm, dev),
-                 x8=torch.empty((M, K), dtype=torch.int8, device=dev),
+                 x8=qoq.empty_act(M, K, dev),
                  s_x=torch.empty(M, dtype=torch.float32, device=dev),
                  y=torch.empty((M, N), dtype=torch.float16, device=dev))
         c["act"] = ActCall(qoq, torch, c["x"], c["x8"], c["s_x"])

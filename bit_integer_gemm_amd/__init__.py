@@ -7,8 +7,13 @@ is visible the calls raise.
 
 Low-level names mirror the C ABI in include/qoq.h (``qoq_pack_weights``,
 ``qoq_quantize_act``, ``qoq_w4a8_gemm``, ``qoq_packed_weight_bytes``,
-``qoq_gemm_workspace_bytes``, ``qoq_status_string``); ``pack_weights``,
-``quantize_act`` and ``w4a8_gemm`` are the tensor-level conveniences.
+``qoq_act_bytes``, ``qoq_gemm_workspace_bytes``, ``qoq_status_string``);
+``pack_weights``, ``quantize_act`` and ``w4a8_gemm`` are the tensor-level
+conveniences.
+
+The INT8 activations travel in the library's activation tile layout: a
+tensor of shape (ceil(M/16), K/16, 16, 16) whose element [t, j, r, b] is the
+code of token 16t + r, input 16j + b (rows past M are never written).
 """
 from __future__ import annotations
 
@@ -21,10 +26,10 @@ import torch
 
 __all__ = [
     "LIB_PATH", "QoQError", "lib", "GROUP", "PACK_FROM_CANONICAL",
-    "qoq_packed_weight_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
+    "qoq_packed_weight_bytes", "qoq_act_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
     "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string",
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
-    "Workspace",
+    "Workspace", "empty_act",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -64,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_uint32, ctypes.c_size_t)
         L.qoq_packed_weight_bytes.argtypes = [i64, i64, i32]
         L.qoq_packed_weight_bytes.restype = sz
+        L.qoq_act_bytes.argtypes = [i64, i64]
+        L.qoq_act_bytes.restype = sz
         L.qoq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qoq_gemm_workspace_bytes.restype = sz
         L.qoq_pack_weights.argtypes = [vp, i64, i64, i32, vp, vp, ctypes.POINTER(_Canonical),
@@ -88,6 +95,10 @@ def qoq_status_string(status: int) -> str:
 
 def qoq_packed_weight_bytes(N: int, K: int, group: int = GROUP) -> int:
     return int(lib().qoq_packed_weight_bytes(N, K, group))
+
+
+def qoq_act_bytes(M: int, K: int) -> int:
+    return int(lib().qoq_act_bytes(M, K))
 
 
 def qoq_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -188,15 +199,33 @@ def pack_canonical(q4: torch.Tensor, s2: torch.Tensor, z: torch.Tensor, s1: torc
     return PackedWeight(packed, s1, N, K, group, q4, s2, z)
 
 
+def empty_act(M: int, K: int, device) -> torch.Tensor:
+    """An uninitialized x8 buffer for M tokens of K inputs (activation tile
+    layout, shape (ceil(M/16), K/16, 16, 16))."""
+    return torch.empty(((M + 15) // 16, K // 16, 16, 16), dtype=torch.int8, device=device)
+
+
+def _check_act(x8: torch.Tensor, M: int, K: int):
+    _need_gpu(x8, "x8", torch.int8)
+    if tuple(x8.shape) != ((M + 15) // 16, K // 16, 16, 16):
+        raise ValueError(f"x8 must have the activation tile shape {((M + 15) // 16, K // 16, 16, 16)}"
+                         f" for M={M}, K={K}; got {tuple(x8.shape)}")
+
+
 def quantize_act(x: torch.Tensor, out=None):
-    """Per-token INT8 quantization of x fp16 [M, K] -> (x8 int8, s_x fp32)."""
+    """Per-token INT8 quantization of x fp16 [M, K] -> (x8 int8 in the
+    activation tile layout, s_x fp32 [M])."""
     _need_gpu(x, "x", torch.float16)
     M, K = x.shape
     if out is None:
-        x8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        x8 = empty_act(M, K, x.device)
         s_x = torch.empty(M, dtype=torch.float32, device=x.device)
     else:
         x8, s_x = out
+        _check_act(x8, M, K)
+        _need_gpu(s_x, "s_x", torch.float32)
+        if s_x.shape != (M,):
+            raise ValueError(f"s_x must have shape ({M},)")
     _check(qoq_quantize_act(x.data_ptr(), M, K, x8.data_ptr(), s_x.data_ptr(),
                             _stream(x.device)), "qoq_quantize_act")
     return x8, s_x
@@ -232,12 +261,13 @@ def _default_workspace(device: torch.device) -> Workspace:
 
 def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
               y: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
-    """y fp16 [M, N] = fp16(acc * s_x * s1); also returns acc int32 if asked."""
-    _need_gpu(x8, "x8", torch.int8)
+    """y fp16 [M, N] = fp16(acc * s_x * s1) for x8 / s_x from quantize_act
+    (M = len(s_x)); also returns acc int32 if asked."""
     _need_gpu(s_x, "s_x", torch.float32)
-    M, K = x8.shape
-    if K != w.K:
-        raise ValueError(f"x8 has K={K}, weights have K={w.K}")
+    if s_x.dim() != 1:
+        raise ValueError("s_x must be 1-D [M]")
+    M, K = s_x.shape[0], w.K
+    _check_act(x8, M, K)
     dev = x8.device
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.float16, device=dev)

@@ -27,6 +27,11 @@ size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
     return size_t(qoq::packed_layout(N, K).total);
 }
 
+size_t qoq_act_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % qoq::kGroup != 0 || M > kMaxDim || K > kMaxDim) return 0;
+    return size_t(qoq::act_bytes(M, K));
+}
+
 size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
     const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);

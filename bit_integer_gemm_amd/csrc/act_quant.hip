@@ -9,7 +9,8 @@
 // reduction order: a max of exactly converted fp16 values); pass 2 writes the
 // codes from the values still held in registers (rows up to 8192 values) or
 // re-reads the row (longer rows; it is still in the caches). 16-byte loads,
-// 8 fp16 values per lane.
+// 8 fp16 values per lane; the codes go out in the activation tile layout
+// (16-byte chunks of a row 256 bytes apart), 8 bytes per lane.
 #include "qoq_internal.hpp"
 
 #include <hip/hip_fp16.h>
@@ -40,7 +41,7 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
                                                         float* __restrict__ s_x) {
     const int64_t m = blockIdx.x;
     const uint16_t* row = x + m * K;
-    int8_t* out = x8 + m * K;
+    int8_t* out = x8 + act_row_offset(m, K);
     // pass 1: absmax. For finite fp16, |x| ordering equals the ordering of the
     // magnitude bits, so the max is taken on (bits & 0x7fff).
     uint4 v[kRegChunks];
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
         uint2 o;
         o.x = quant_pair(t.x, inv) | (quant_pair(t.y, inv) << 16);
         o.y = quant_pair(t.z, inv) | (quant_pair(t.w, inv) << 16);
-        *reinterpret_cast<uint2*>(out + k) = o;
+        *reinterpret_cast<uint2*>(out + (k >> 4) * kActUnit + (k & 15)) = o;
     };
     if (kInRegs) {
 #pragma unroll

@@ -103,12 +103,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         bptr[cb] = nib + nbc * ng * kBlockBytes + lane * 16;
         rptr[cb] = rec + (nbc * ng8 * kBlockCols + c) * (kRecChunk * 2);
     }
+    // Activations in the tile layout: the A operand of step s of group g for
+    // row tile mt is 1 KiB at tile base + 2048 g + 1024 s, lane l at 16 l.
     // Rows at or beyond M read a valid row instead (the last one): an MFMA
     // row only feeds the same output row, and those rows are never stored.
     // Unpredicated loads keep the prefetch ring free of per-lane branches.
     const int8_t* aptr[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) aptr[mt] = x8 + int64_t(min(16 * mt + c, M - 1)) * K + 16 * h;
+    for (int mt = 0; mt < MT; ++mt)
+        aptr[mt] = x8 + act_row_offset(min(16 * mt + c, M - 1), K) + kActUnit * h;
 
     v4i acc[MT][CB];
 #pragma unroll
@@ -139,7 +142,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                av[p][mt][s] = *reinterpret_cast<const v4i*>(aptr[mt] + g * kGroup + 64 * s);
+                av[p][mt][s] = *reinterpret_cast<const v4i*>(aptr[mt] + g * kActGroupBytes + 1024 * s);
         if (per_group_rec) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
@@ -276,14 +279,15 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
         bptr[cb] = nib + nbc * ng * kBlockBytes + lane * 16;
         rptr[cb] = rec + (nbc * ng8 * kBlockCols + c) * (kRecChunk * 2);
     }
-    // fragment f = wave + NW*j -> (row tile f >> 1, MFMA step f & 1); rows at
-    // or beyond M read the last row (never stored)
+    // fragment f = wave + NW*j -> (row tile f >> 1, MFMA step f & 1), 1 KiB
+    // contiguous in the activation tile layout; rows at or beyond M read the
+    // last row (never stored)
     const int8_t* aptr[AFW];
 #pragma unroll
     for (int j = 0; j < AFW; ++j) {
         const int f = min(wave + NW * j, AF - 1);
         const int row = min(m0 + 16 * (f >> 1) + c, M - 1);
-        aptr[j] = x8 + int64_t(row) * K + 64 * (f & 1) + 16 * h;
+        aptr[j] = x8 + act_row_offset(row, K) + 1024 * (f & 1) + kActUnit * h;
     }
     auto owns = [&](int j) { return wave + NW * j < AF; };
 
@@ -313,7 +317,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
     auto load_a = [&](int p, int g) {
 #pragma unroll
         for (int j = 0; j < AFW; ++j)
-            ar[p][j] = *reinterpret_cast<const v4i*>(aptr[j] + int64_t(g) * kGroup);
+            ar[p][j] = *reinterpret_cast<const v4i*>(aptr[j] + int64_t(g) * kActGroupBytes);
     };
     auto stage_a = [&](int slot, int p) {
 #pragma unroll
@@ -431,8 +435,9 @@ __device__ __forceinline__ void tile_of(int L, int tiles_m, int tiles_n, int& tm
 //     the block of its 16 columns); low nibbles of the two chunks are MFMA
 //     steps 0 and 1 of the group, high nibbles steps 2 and 3 -- the layout
 //     written for the 16x16x64 form serves this instruction unchanged.
-//   * Buffer loads: one per-lane VGPR offset per stream, everything uniform
-//     in SGPRs; out-of-range rows of A read as zero.
+//   * Buffer loads: per-lane VGPR offsets fixed for the whole loop, the
+//     group and step offsets uniform in SGPRs; rows of A past M read the
+//     last row (those outputs are never stored).
 //   * Register budget is kept under 256 (accumulators in AGPRs, shallow
 //     rings) so two workgroups share a CU: one's barrier waits, LDS latency
 //     and dequantization bursts are covered by the other's MFMAs.
@@ -464,12 +469,19 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
     const int nbw = tn * BNB + wave * 2 * CB;     // this wave's first 16-column block
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)x8, (short)0, M * K, 0x00020000);
+        (void*)x8, (short)0, int(act_bytes(M, K)), 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)nib, (short)0, nbt * ng * kBlockBytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)rec, (short)0, nbt * ng8 * (kBlockCols * kRecChunk * 2), 0x00020000);
-    const int a_lane = j * K + 16 * q;
+    // A fragment (32-row tile u, step st) of group g: lanes 0-31 take rows
+    // 0-31 of the tile at inputs 32st .. +15, lanes 32-63 the next 16 inputs;
+    // in the tile layout that is two 512-byte runs. Rows at or beyond M read
+    // the last row (never stored).
+    int a_lane[AFW];
+#pragma unroll
+    for (int u = 0; u < AFW; ++u)
+        a_lane[u] = int(act_row_offset(min(m0 + 32 * u + j, M - 1), K)) + kActUnit * q;
     int b_lane[CB], r_lane[CB];
 #pragma unroll
     for (int t = 0; t < CB; ++t) {
@@ -503,9 +515,9 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
         g = min(g, ng - 1);
 #pragma unroll
         for (int u = 0; u < AFW; ++u) {
-            const int f = wave + 4 * u;
-            const int soff = (m0 + 32 * (f >> 2)) * K + g * kGroup + 32 * (f & 3);
-            ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane, soff, 0));
+            // fragment f = wave + 4u: row tile u, step wave
+            const int soff = g * kActGroupBytes + 2 * kActUnit * wave;
+            ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane[u], soff, 0));
         }
     };
     auto stage_a = [&](int slot) {
@@ -652,7 +664,7 @@ __global__ void __launch_bounds__(256) gemm_generic_kernel(
     for (int mt = 0; mt < MT; ++mt) {
         const int r = m0 + 16 * mt + c;
         aval[mt] = r < M;
-        arow[mt] = x8 + int64_t(aval[mt] ? r : 0) * K + 16 * h;
+        arow[mt] = x8 + act_row_offset(aval[mt] ? r : 0, K) + kActUnit * h;
     }
     v4i acc[MT][CB];
 #pragma unroll
@@ -676,7 +688,7 @@ __global__ void __launch_bounds__(256) gemm_generic_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                a[mt][s] = aval[mt] ? *reinterpret_cast<const v4i*>(arow[mt] + g * kGroup + 64 * s)
+                a[mt][s] = aval[mt] ? *reinterpret_cast<const v4i*>(arow[mt] + int64_t(g) * kActGroupBytes + 1024 * s)
                                     : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -756,7 +768,7 @@ hipError_t launch_generic(const GemmPlan& p, const Args& a, hipStream_t stream) 
     X(2, 1, 16, 2) X(2, 1, 8, 2) X(2, 2, 8, 2) X(2, 2, 4, 2) X(2, 4, 4, 2)            \
     X(2, 4, 2, 2) X(2, 8, 2, 2) X(2, 2, 8, 4) X(2, 4, 4, 4)                           \
     X(4, 1, 8, 2) X(4, 2, 8, 2) X(4, 2, 4, 2) X(4, 4, 4, 2) X(4, 4, 2, 2)             \
-    X(4, 4, 4, 4)
+    X(4, 4, 4, 4) X(4, 1, 8, 4) X(2, 1, 8, 4) X(1, 1, 8, 4) X(2, 1, 16, 4)
 
 // Every compiled shared-activation configuration: (MT, CB, NW, P).
 #define QOQ_LDS_CONFIGS(X)                                                           \
@@ -814,18 +826,19 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     p.splits = 1;
     p.groups_per_split = int(ng);
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    // 32-bit buffer offsets: the fast families need N*K/2 and M*K below 2^31
-    const bool small_offsets = N * K / 2 < (int64_t(1) << 31) && M * K < (int64_t(1) << 31);
+    // 32-bit buffer offsets: the fast families need the nibble and x8 buffer
+    // sizes below 2^31
+    const bool small_offsets = N * K / 2 < (int64_t(1) << 31) && act_bytes(M, K) < (int64_t(1) << 31);
     if (!small_offsets) {
         p.kind = 0;
         p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         p.cb = 2;
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
-        if (p.mt == 1) { p.cb = 1; p.kw = 16; p.pd = 4; }
-        else if (p.mt == 2) { p.cb = 1; p.kw = 8; p.pd = 2; }
+        if (p.mt == 1) { p.cb = 1; p.kw = 8; p.pd = 4; }
+        else if (p.mt == 2) { p.cb = 1; p.kw = 8; p.pd = 4; }
         else if (nbt >= 512) { p.cb = 2; p.kw = 4; p.pd = 2; }
-        else { p.cb = 1; p.kw = 8; p.pd = 2; }
+        else { p.cb = 1; p.kw = 8; p.pd = 4; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
     } else if (M <= 64) {
@@ -839,7 +852,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.pa = 2;   // workgroups per CU
         const int64_t t42 = ((M + 127) / 128) * ((nbt + 15) / 16);
         const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
-        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 1; }
+        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
         else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
         else { p.mt = 2; p.cb = 1; p.pd = 2; }
     }

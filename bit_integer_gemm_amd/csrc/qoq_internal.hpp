@@ -23,6 +23,15 @@
 //       (s2, 128 - z*s2) as two uint8 per (channel, group); one 16-byte load
 //       gives a lane the records of 8 consecutive groups of its channel.
 //       Entries for groups >= NG are zero.
+//
+// Activation tile layout, version 1 (what the activation quantizer writes and
+// the GEMM kernels read): code (m, k) of x8 at byte
+//   ((m >> 4) * (K >> 4) + (k >> 4)) * 256 + (m & 15) * 16 + (k & 15),
+// i.e. row m starts at (m >> 4) * 16K + (m & 15) * 16 and its 16-byte chunk
+// j sits 256 bytes after chunk j - 1. Group g of a 16-row tile is 2 KiB
+// contiguous; its half s (inputs 64s .. 64s + 63) is the 1 KiB A operand of
+// one v_mfma_i32_16x16x64_i8 step, lane l at byte 16 l. Rows past M in the
+// last tile are never written or read (loads clamp the row to M - 1).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,6 +68,19 @@ constexpr int kRecChunk = 8;
 constexpr int kRecChunkBytes = kBlockCols * kRecChunk * 2;  // 256
 constexpr int kProtect = 119;   // level-1 protective range
 constexpr int kActMax = 127;    // activation code bound
+constexpr int kActTileRows = 16;
+constexpr int kActUnit = 256;                          // 16 rows x 16 bytes
+constexpr int kActGroupBytes = kActUnit * kGroup / 16; // 2048: one group of a row tile
+
+// Bytes of the x8 buffer (activation tile layout) for M rows of K inputs.
+__host__ __device__ inline int64_t act_bytes(int64_t M, int64_t K) {
+    return (M + kActTileRows - 1) / kActTileRows * kActTileRows * K;
+}
+
+// Byte offset of the first code of row m (valid on host and device).
+__host__ __device__ inline int64_t act_row_offset(int64_t m, int64_t K) {
+    return (m >> 4) * 16 * K + (m & 15) * 16;
+}
 
 struct PackedLayout {
     int64_t nb, ng, ng8;

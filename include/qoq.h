@@ -68,6 +68,18 @@ typedef enum qoq_status {
  * canonical (q4, s2, z) as they are. */
 #define QOQ_PACK_FROM_CANONICAL 0x1u
 
+/* Activation tile layout (version 1) of the INT8 activations x8 that
+ * qoq_quantize_act writes and qoq_w4a8_gemm reads. Rows are grouped in tiles
+ * of 16 and each row in 16-byte chunks; code (m, k) is at byte
+ *     ((m / 16) * (K / 16) + k / 16) * 256 + (m % 16) * 16 + k % 16,
+ * so one 256-byte unit holds a 16-row x 16-input block, row-major. Four
+ * consecutive units are one v_mfma_i32_16x16x64_i8 A operand (lane l reads
+ * bytes 16 l .. 16 l + 15) and a v_mfma_i32_32x32x32_i8 A operand is two
+ * 512-byte runs: every activation load reads whole cache lines. The buffer
+ * holds qoq_act_bytes(M, K) bytes; the bytes of rows M .. 16*ceil(M/16) - 1
+ * are never written and never read. */
+#define QOQ_ACT_LAYOUT_VERSION 1
+
 /* Canonical level-2 output / input, all device pointers, row-major:
  *   q4 [N*K]        one UINT4 code per byte (0..15), element (n, k) at n*K + k
  *   s2 [N*K/128]    group scale, int8 in 1..16, group (n, g) at n*(K/128) + g
@@ -87,6 +99,11 @@ typedef struct qoq_canonical {
  * (s2, 128 - z*s2) byte pairs. Returns 0 for invalid shapes (N <= 0,
  * K <= 0, N % 16 != 0, K % group != 0, group != 128). Host-only. */
 size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group);
+
+/* Bytes of the x8 buffer for M tokens of K inputs in the activation tile
+ * layout: 16 * ceil(M / 16) * K. Returns 0 for M <= 0 and for invalid K
+ * (K <= 0, K % 128 != 0). Host-only. */
+size_t qoq_act_bytes(int64_t M, int64_t K);
 
 /* Progressive group quantization and compute-aware packing (offline).
  * Pages: velog notes "Methods / 1) Algorithm: QoQ" (8-bit with per-channel
@@ -112,7 +129,8 @@ qoq_status qoq_pack_weights(const float* W, int64_t N, int64_t K, int32_t group,
  * Pages: QServe abstract (8-bit activations); velog notes "Background"
  * (per-token activation scale next to per-channel weight scale).
  *   x    [M,K] fp16 bits, row-major.   M >= 0, K > 0, K % 128 == 0.
- *   x8   out [M,K] int8.               s_x  out [M] fp32.
+ *   x8   out, qoq_act_bytes(M, K) bytes: the int8 codes in the activation
+ *        tile layout (above).           s_x  out [M] fp32.
  * Row m: a = max|x[m,:]|; s_x = fp32(a/127); x8 = clamp(rne(x * fp32(127/a)),
  * -127, 127); a zero row gives s_x = 0 and zero codes. M == 0 launches
  * nothing. Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN, QOQ_ERR_HIP. */
@@ -133,7 +151,8 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * parallel INT4->INT8 dequantization, subtraction after multiplication) and
  * "Background" (partial-sum dequantization in the main loop is the cost to
  * avoid); "Part5 LLM部署技术" section 3 (no partial-sum dequantization).
- *   x8, s_x      from qoq_quantize_act: [M,K] int8, [M] fp32.
+ *   x8, s_x      from qoq_quantize_act: int8 codes in the activation tile
+ *                layout (qoq_act_bytes(M, K) bytes), [M] fp32.
  *   M >= 0, K > 0, K % 128 == 0, N > 0, N % 16 == 0, group == 128.
  *   packed, s1   from qoq_pack_weights for the same N, K.
  *   y            out [M,N] fp16 bits, row-major: fp16(acc * s_x[m] * s1[n]).

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -27,7 +28,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) >= {"qoq_pack_weights", "qoq_quantize_act", "qoq_w4a8_gemm",
                           "qoq_packed_weight_bytes", "qoq_gemm_workspace_bytes",
-                          "qoq_status_string"}
+                          "qoq_act_bytes", "qoq_status_string"}
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -47,6 +48,32 @@ def test_packed_weight_bytes():
     for bad in [(0, 128), (16, 0), (8, 128), (16, 64), (-16, 128), (16, 200)]:
         assert qoq.qoq_packed_weight_bytes(*bad) == 0
     assert qoq.qoq_packed_weight_bytes(16, 128, 64) == 0
+
+
+def test_act_bytes():
+    # rows padded to tiles of 16, K bytes per row
+    assert qoq.qoq_act_bytes(1, 4096) == 16 * 4096
+    assert qoq.qoq_act_bytes(16, 128) == 16 * 128
+    assert qoq.qoq_act_bytes(17, 256) == 32 * 256
+    assert qoq.qoq_act_bytes(4096, 4096) == 4096 * 4096
+    for bad in [(0, 128), (-1, 128), (4, 0), (4, 100), (4, -128)]:
+        assert qoq.qoq_act_bytes(*bad) == 0
+
+
+def test_act_layout_formula_is_a_bijection():
+    # the documented tile layout maps the M x K codes one-to-one into the
+    # first 16*ceil(M/16)*K bytes, and act_rows inverts it
+    from act_layout import act_offset, act_rows
+    M, K = 37, 384
+    size = qoq.qoq_act_bytes(M, K)
+    m, k = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    off = act_offset(m, k, K)
+    assert off.min() >= 0 and off.max() < size
+    assert len(np.unique(off)) == M * K
+    codes = np.arange(M * K, dtype=np.int64).reshape(M, K)
+    buf = np.full(size, -1, np.int64)
+    buf[off.ravel()] = codes.ravel()
+    assert np.array_equal(act_rows(buf.reshape(-1, K // 16, 16, 16), M), codes)
 
 
 def test_workspace_bytes():

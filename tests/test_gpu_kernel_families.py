@@ -23,7 +23,7 @@ DECODE = [(1, 1, 16, 2), (1, 1, 8, 2), (1, 2, 8, 2), (1, 2, 4, 2), (1, 4, 4, 2),
           (1, 8, 2, 2), (1, 1, 16, 4), (1, 2, 8, 4), (1, 4, 4, 4), (2, 1, 16, 2), (2, 1, 8, 2),
           (2, 2, 8, 2), (2, 2, 4, 2), (2, 4, 4, 2), (2, 4, 2, 2), (2, 8, 2, 2), (2, 2, 8, 4),
           (2, 4, 4, 4), (4, 1, 8, 2), (4, 2, 8, 2), (4, 2, 4, 2), (4, 4, 4, 2), (4, 4, 2, 2),
-          (4, 4, 4, 4)]
+          (4, 4, 4, 4), (4, 1, 8, 4), (2, 1, 8, 4), (1, 1, 8, 4), (2, 1, 16, 4)]
 LDS = [(1, 1, 4, 2), (1, 2, 4, 2), (1, 1, 8, 2), (1, 2, 8, 2), (1, 4, 4, 2), (2, 1, 4, 2),
        (2, 2, 4, 2), (2, 1, 8, 2), (2, 2, 8, 2), (2, 4, 4, 2), (4, 1, 4, 2), (4, 2, 4, 2),
        (4, 1, 8, 2), (4, 2, 8, 2), (4, 4, 4, 2), (4, 1, 4, 4), (4, 2, 4, 4), (4, 1, 8, 4),

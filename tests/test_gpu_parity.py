@@ -17,6 +17,7 @@ import torch
 
 import oracle
 import workloads as wl
+from act_layout import act_rows
 
 qoq = pytest.importorskip("bit_integer_gemm_amd")
 
@@ -66,7 +67,7 @@ def full_check(W, X):
     ref = oracle.w4a8_linear(X, W)
     rows = torch.arange(W.shape[0], device=DEV)
     check_canonical(pw, W, rows)
-    assert np.array_equal(x8.cpu().numpy(), ref["x8"]), "x8"
+    assert np.array_equal(act_rows(x8, X.shape[0]), ref["x8"]), "x8"
     assert np.array_equal(s_x.cpu().numpy().view(np.uint32), ref["s_x"].view(np.uint32)), "s_x"
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"]), "acc"
     return check_y(y.cpu().numpy().astype(np.float64), ref["y"])
@@ -85,7 +86,7 @@ def sampled_check(W, X, pw, x8, s_x, y, acc, n_cols=96, n_rows=64, seed=0):
     q = check_canonical(pw, W[cols], torch.from_numpy(cols).to(DEV))
     w8 = oracle.dequantize_level2(q["q4"], q["s2"], q["z"], wl.GROUP)
     x8_ref, sx_ref = oracle.quantize_act(X[toks])
-    assert np.array_equal(x8.cpu().numpy()[toks], x8_ref), "x8"
+    assert np.array_equal(act_rows(x8, M)[toks], x8_ref), "x8"
     assert np.array_equal(s_x.cpu().numpy()[toks].view(np.uint32), sx_ref.view(np.uint32)), "s_x"
     acc_ref = oracle.int_gemm_fp64(x8_ref, w8)
     t_idx = torch.from_numpy(toks).to(DEV)
@@ -140,7 +141,7 @@ def test_identity_canonical_packing():
     _, X, _ = wl.make_inputs(M, K, 16, seed=5)
     Xd = torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV)
     x8, s_x = qoq.quantize_act(Xd)
-    x8_h = x8.cpu().numpy()
+    x8_h = act_rows(x8, M)
     x8_ref, sx_ref = oracle.quantize_act(X)
     assert np.array_equal(x8_h, x8_ref)
     for zero in (0, 8):
@@ -183,12 +184,12 @@ def test_hand_cases_padded():
 def test_empty_batch_is_a_no_op():
     W, _, _ = wl.make_inputs(1, 256, 32, seed=1)
     pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
-    x8 = torch.empty((0, 256), dtype=torch.int8, device=DEV)
+    x8 = qoq.empty_act(0, 256, DEV)
     s_x = torch.empty(0, dtype=torch.float32, device=DEV)
     y = qoq.w4a8_gemm(x8, s_x, pw)
     assert y.shape == (0, 32)
     x8b, sxb = qoq.quantize_act(torch.empty((0, 256), dtype=torch.float16, device=DEV))
-    assert x8b.shape == (0, 256)
+    assert x8b.shape == (0, 16, 16, 16) and sxb.shape == (0,)
 
 
 def test_workspace_is_reusable():

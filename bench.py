@@ -5,7 +5,8 @@
 One step = the run-time hot path over the decode-shaped workload: for every
 batch size M in {1, 8, 32, 64} (K = N = 4096, group 128), per-token INT8
 quantization of the fp16 activations followed by the W4A8 GEMM with its
-fused fp16 epilogue. The weights are quantized and packed once before timing
+fused fp16 epilogue, as one qoq_w4a8_linear call (a single fused kernel for
+M <= 8, the quantizer and the GEMM for larger M). The weights are quantized and packed once before timing
 (they are static in serving); that offline step is timed separately under
 "pack". Each GEMM launch reads a different copy of the packed weights and
 the copies together exceed 512 MiB, twice the 256 MiB last-level cache, so
@@ -15,8 +16,9 @@ Timing: each step is captured once per weight copy set into a HIP graph; K
 graph launches are timed with events on the capture stream. While the host
 enqueues, a spin kernel keeps the GPU busy, so launch overhead on the host
 never shows up as idle GPU time inside the timed region. Per-kernel
-durations of the GEMM (the dominant kernel) are taken the same way: one event
-pair around many back-to-back launches, divided by their number.
+durations of the GEMM kernels (the dominant kernels: the fused kernel for
+M <= 8, the GEMM for larger M) are taken the same way: one event pair around
+many back-to-back launches, divided by their number.
 
 The other workloads (Llama-3-8B layers at M=256, the M=4096 prefill GEMM,
 Qwen1.5-72B layers at M=64 and M=1024) are timed GEMM by GEMM and listed
@@ -173,6 +175,33 @@ class ActCall:
             raise RuntimeError(f"qoq_quantize_act failed with status {st}")
 
 
+class LinearCall:
+    """A prepared qoq_w4a8_linear call (activation quantization + GEMM)."""
+
+    def __init__(self, qoq, torch, x, packed, s1, N, y, ws):
+        M, K = x.shape
+        self.f = qoq.lib().qoq_w4a8_linear
+        wsb = qoq.qoq_linear_workspace_bytes(M, N, K)
+        wsp = None
+        if wsb:
+            buf = ws.get(wsb)
+            wsp, wsb = buf.data_ptr(), buf.numel()
+        self.args = (x.data_ptr(), M, K, packed.data_ptr(), s1.data_ptr(), N, 128, y.data_ptr(),
+                     None, wsp, wsb)
+        self.torch = torch
+
+    def __call__(self):
+        st = self.f(*self.args, self.torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise RuntimeError(f"qoq_w4a8_linear failed with status {st}")
+
+
+def fused_bytes(M, K, N, group=wl.GROUP):
+    """HBM bytes the fused kernel must move: the weights as for the GEMM,
+    the fp16 activations (no INT8 copy, no token scales) and the output."""
+    return N * K // 2 + (N * K // group) * 3 // 2 + 2 * N + 2 * M * K + 2 * M * N
+
+
 def traffic_record():
     """HBM bytes per decode GEMM launch from the committed rocprofv3 counter
     runs, if they were taken on the current GEMM source; else None."""
@@ -218,23 +247,21 @@ def main():
         c = dict(M=M, x=to_half_device(torch, Xm, dev),
                  x8=qoq.empty_act(M, K, dev),
                  s_x=torch.empty(M, dtype=torch.float32, device=dev),
-                 y=torch.empty((M, N), dtype=torch.float16, device=dev))
+                 y=torch.empty((M, N), dtype=torch.float16, device=dev),
+                 fused=qoq.qoq_linear_workspace_bytes(M, N, K) == 0)
         c["act"] = ActCall(qoq, torch, c["x"], c["x8"], c["s_x"])
         per_m.append(c)
-    # step j uses copies [n_m*j, n_m*j + n_m)
+    # step j uses copies [n_m*j, n_m*j + n_m); each M is one qoq_w4a8_linear
+    # call: a single fused launch for M <= 8, quantizer + GEMM otherwise
     n_phase = len(copies) // n_m
     phases = []
     for j in range(n_phase):
-        calls = []
-        for i, c in enumerate(per_m):
-            calls.append((c["act"], GemmCall(qoq, torch, c["x8"], c["s_x"], copies[n_m * j + i],
-                                             pw.s1, N, c["y"], ws)))
-        phases.append(calls)
+        phases.append([LinearCall(qoq, torch, c["x"], copies[n_m * j + i], pw.s1, N, c["y"], ws)
+                       for i, c in enumerate(per_m)])
 
     def eager_step(j):
-        for act, gemm in phases[j % n_phase]:
-            act()
-            gemm()
+        for lin in phases[j % n_phase]:
+            lin()
 
     # capture the step into HIP graphs of G consecutive steps (G divides both
     # the step count and the number of weight-copy phases), on torch's
@@ -278,23 +305,51 @@ def main():
     ops_step = sum(wl.algorithmic_ops(c["M"], K, N) for c in per_m)
     value_tops = ops_step / step_s / 1e12
 
-    # per-launch durations of the dominant kernel (GEMM, rotating over the
-    # weight copies like the step does) and of the activation quantizer
+    # per-launch durations of the dominant kernel, rotating over the weight
+    # copies like the step does: the fused kernel for M <= 8, the GEMM
+    # kernel (on the quantizer's output) for larger M; and the quantizer
     iters = max(128, n_phase)
-    gemm_t = per_launch_times(torch, blocker,
-                              [[phases[j][i][1] for j in range(n_phase)] for i in range(n_m)],
-                              iters)
-    act_t = per_launch_times(torch, blocker, [c["act"] for c in per_m], iters)
-    gemm_bytes = [wl.algorithmic_bytes(c["M"], K, N) for c in per_m]
-    achieved = sum(gemm_bytes) / sum(gemm_t) / 1e9
+    kern = []
+    for i, c in enumerate(per_m):
+        if c["fused"]:
+            kern.append([phases[j][i] for j in range(n_phase)])
+        else:
+            c["act"]()
+            kern.append([GemmCall(qoq, torch, c["x8"], c["s_x"], copies[n_m * j + i], pw.s1, N,
+                                  c["y"], ws) for j in range(n_phase)])
+    kern_t = per_launch_times(torch, blocker, kern, iters)
+    # the plain GEMM kernel on the quantizer's output, also for the fused M
+    # (the two-call path of the same step), for comparison
+    for c in per_m:
+        c["act"]()
+    gemm_only_t = per_launch_times(
+        torch, blocker, [[GemmCall(qoq, torch, c["x8"], c["s_x"], copies[n_m * j + i], pw.s1, N,
+                                   c["y"], ws) for j in range(n_phase)]
+                         for i, c in enumerate(per_m)], iters)
+    gemm_only_achieved = (sum(wl.algorithmic_bytes(c["M"], K, N) for c in per_m) /
+                          sum(gemm_only_t) / 1e9)
+    unfused = [c for c in per_m if not c["fused"]]
+    act_t = dict(zip([c["M"] for c in unfused],
+                     per_launch_times(torch, blocker, [c["act"] for c in unfused], iters)))
+    lin_t = per_launch_times(torch, blocker, [[phases[j][i] for j in range(n_phase)]
+                                              for i in range(n_m)], iters)
+    kern_bytes = [fused_bytes(c["M"], K, N) if c["fused"] else wl.algorithmic_bytes(c["M"], K, N)
+                  for c in per_m]
+    achieved = sum(kern_bytes) / sum(kern_t) / 1e9
     shapes_out = []
-    for c, t, ta, b in zip(per_m, gemm_t, act_t, gemm_bytes):
+    for c, t, tl, b, tg in zip(per_m, kern_t, lin_t, kern_bytes, gemm_only_t):
         ops = wl.algorithmic_ops(c["M"], K, N)
-        shapes_out.append(dict(workload="decode", shape="square", M=c["M"], K=K, N=N,
-                               gemm_us=round(t * 1e6, 3), act_quant_us=round(ta * 1e6, 3),
-                               tops=round(ops / t / 1e12, 3), gbs=round(b / t / 1e9, 1),
-                               hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                               mfma_frac=round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)))
+        rec = dict(workload="decode", shape="square", M=c["M"], K=K, N=N,
+                   path="fused" if c["fused"] else "two-call",
+                   gemm_us=round(t * 1e6, 3))
+        if not c["fused"]:
+            rec["act_quant_us"] = round(act_t[c["M"]] * 1e6, 3)
+        else:
+            rec["gemm_only_us"] = round(tg * 1e6, 3)
+        rec.update(linear_us=round(tl * 1e6, 3), tops=round(ops / t / 1e12, 3),
+                   gbs=round(b / t / 1e9, 1), hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                   mfma_frac=round(ops / t / 1e12 / INT8_PEAK_TOPS, 4))
+        shapes_out.append(rec)
 
     # streaming-copy reference (a plain elementwise kernel: read N bytes, write
     # N bytes) of the decode weight size and of 1 GiB; its counters calibrate
@@ -356,14 +411,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode-shaped W4A8 GEMM step: per-token INT8 activation "
                                "quantization + W4A8 GEMM for M in {1,8,32,64}, K=N=4096, "
-                               "group 128, weights HBM-resident (rotated copies)",
+                               "group 128, weights HBM-resident (rotated copies); one "
+                               "qoq_w4a8_linear call per M (fused kernel for M<=8)",
                    "M": list(dw.Ms), "K": K, "N": N, "group": 128,
                    "weight_copies": n_phase * n_m},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "kernel": "W4A8 GEMM over the step's four launches (M=1,8,32,64): "
-                               "algorithmic bytes / mean event-timed launch duration"},
+                     "kernel": "W4A8 GEMM kernels of the step (fused quantize+GEMM for "
+                               "M=1,8; GEMM for M=32,64): sum of algorithmic bytes / sum of "
+                               "mean event-timed launch durations"},
+        "gemm_only_roofline": {"achieved": round(gemm_only_achieved, 1),
+                               "frac": round(gemm_only_achieved / HBM_PEAK_GBS, 4),
+                               "kernel": "the GEMM kernel alone on quantized input, M=1,8,32,64 "
+                                         "(two-call path)"},
         "cpu_baseline": cpu,
         "step_eager_ms": round(eager_step_s * 1e3, 6),
         "steps_per_graph": G,

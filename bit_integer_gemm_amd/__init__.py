@@ -7,8 +7,9 @@ is visible the calls raise.
 
 Low-level names mirror the C ABI in include/qoq.h (``qoq_pack_weights``,
 ``qoq_quantize_act``, ``qoq_w4a8_gemm``, ``qoq_packed_weight_bytes``,
-``qoq_act_bytes``, ``qoq_gemm_workspace_bytes``, ``qoq_status_string``);
-``pack_weights``, ``quantize_act`` and ``w4a8_gemm`` are the tensor-level
+``qoq_act_bytes``, ``qoq_gemm_workspace_bytes``, ``qoq_w4a8_linear``,
+``qoq_linear_workspace_bytes``, ``qoq_status_string``); ``pack_weights``,
+``quantize_act``, ``w4a8_gemm`` and ``w4a8_linear`` are the tensor-level
 conveniences.
 
 The INT8 activations travel in the library's activation tile layout: a
@@ -27,9 +28,10 @@ import torch
 __all__ = [
     "LIB_PATH", "QoQError", "lib", "GROUP", "PACK_FROM_CANONICAL",
     "qoq_packed_weight_bytes", "qoq_act_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
-    "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string",
+    "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string", "qoq_w4a8_linear",
+    "qoq_linear_workspace_bytes",
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
-    "Workspace", "empty_act",
+    "Workspace", "empty_act", "w4a8_linear",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -80,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.qoq_quantize_act.restype = ctypes.c_int
         L.qoq_w4a8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.qoq_w4a8_gemm.restype = ctypes.c_int
+        L.qoq_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.qoq_linear_workspace_bytes.restype = sz
+        L.qoq_w4a8_linear.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
+        L.qoq_w4a8_linear.restype = ctypes.c_int
         L.qoq_status_string.argtypes = [ctypes.c_int]
         L.qoq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -120,6 +126,16 @@ def qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
                   workspace_bytes, stream) -> int:
     return lib().qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
                                workspace_bytes, stream)
+
+
+def qoq_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().qoq_linear_workspace_bytes(M, N, K))
+
+
+def qoq_w4a8_linear(x, M, K, packed, s1, N, group, y, acc_debug, workspace, workspace_bytes,
+                    stream) -> int:
+    return lib().qoq_w4a8_linear(x, M, K, packed, s1, N, group, y, acc_debug, workspace,
+                                 workspace_bytes, stream)
 
 
 # ---------------------------------------------------------------------------
@@ -232,11 +248,9 @@ def quantize_act(x: torch.Tensor, out=None):
 
 
 class Workspace:
-    """A zero-filled device buffer for split-K partial sums, grown on demand.
-
-    The library returns it to zero after every completed call, so one buffer
-    serves any number of sequential calls on one stream.
-    """
+    """A zero-filled device buffer, grown on demand, for the workspace
+    arguments of qoq_w4a8_gemm and qoq_w4a8_linear. One buffer serves any
+    number of sequential calls on one stream."""
 
     def __init__(self, device):
         self.device = torch.device(device)
@@ -281,4 +295,30 @@ def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: b
     _check(qoq_w4a8_gemm(x8.data_ptr(), s_x.data_ptr(), M, K, w.packed.data_ptr(),
                          w.s1.data_ptr(), w.N, w.group, y.data_ptr(), _ptr(acc), ws_ptr,
                          ws_bytes, _stream(dev)), "qoq_w4a8_gemm")
+    return (y, acc) if acc_debug else y
+
+
+def w4a8_linear(x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
+                y: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """y fp16 [M, N] from fp16 activations x [M, K] in one call: per-token
+    quantization and the W4A8 GEMM (one fused launch for small M, otherwise
+    the quantizer into the workspace and the GEMM); also returns acc int32
+    if asked."""
+    _need_gpu(x, "x", torch.float16)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, weights have K={w.K}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float16, device=dev)
+    acc = torch.empty((M, w.N), dtype=torch.int32, device=dev) if acc_debug else None
+    ws_bytes = qoq_linear_workspace_bytes(M, w.N, K) if M > 0 else 0
+    ws_ptr = None
+    if ws_bytes:
+        ws = (workspace or _default_workspace(dev)).get(ws_bytes)
+        ws_ptr = ws.data_ptr()
+        ws_bytes = ws.numel()
+    _check(qoq_w4a8_linear(x.data_ptr(), M, K, w.packed.data_ptr(), w.s1.data_ptr(), w.N,
+                           w.group, y.data_ptr(), _ptr(acc), ws_ptr, ws_bytes, _stream(dev)),
+           "qoq_w4a8_linear")
     return (y, acc) if acc_debug else y

@@ -104,6 +104,42 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
+size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
+    const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);
+    return plan.valid ? size_t(plan.ws_bytes) : 0;
+}
+
+qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const void* packed,
+                           const uint16_t* s1, int64_t N, int32_t group, uint16_t* y,
+                           int32_t* acc_debug, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    const qoq_status st = check_weight_shape(N, K, group);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(x) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
+    const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);
+    if (!plan.valid) return QOQ_ERR_CONFIG;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* pk = static_cast<const uint8_t*>(packed);
+    if (plan.fused) {
+        const hipError_t e = qoq::launch_linear_fused(plan, x, M, K, pk, s1, N, y, acc_debug, s);
+        return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+    }
+    if (workspace == nullptr || workspace_bytes < size_t(plan.ws_bytes)) return QOQ_ERR_WORKSPACE;
+    if (misaligned(workspace)) return QOQ_ERR_ALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int8_t* x8 = reinterpret_cast<int8_t*>(ws + plan.x8_offset);
+    float* s_x = reinterpret_cast<float*>(ws + plan.sx_offset);
+    hipError_t e = qoq::launch_quantize_act(x, M, K, x8, s_x, s);
+    if (e != hipSuccess) return QOQ_ERR_HIP;
+    e = qoq::launch_gemm(plan.gemm, x8, s_x, M, K, pk, s1, N, y, acc_debug,
+                         plan.gemm.ws_bytes > 0 ? ws + plan.gemm_ws_offset : nullptr, s);
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
 const char* qoq_status_string(int status) {
     switch (status) {
         case QOQ_OK: return "ok";

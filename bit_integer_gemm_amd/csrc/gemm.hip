@@ -113,6 +113,26 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
     for (int mt = 0; mt < MT; ++mt)
         aptr[mt] = x8 + act_row_offset(min(16 * mt + c, M - 1), K) + kActUnit * h;
 
+    // Epilogue elements of this thread (see the end): their token and
+    // channel scales are fetched now, so the epilogue waits for no load.
+    // Output element e = (mt, r, h, cb, c) is token 16mt + 4h + r, channel
+    // 16(nb0 + cb) + c; consecutive threads take consecutive channels.
+    constexpr int E = MT * 16 * CB * 16;
+    constexpr int EI = (E + 64 * KW - 1) / (64 * KW);
+    float esx[EI], esw[EI];
+#pragma unroll
+    for (int it = 0; it < EI; ++it) {
+        const int e = min(int(threadIdx.x) + it * 64 * KW, E - 1);
+        const int cc = e & 15;
+        const int t = e >> 4;
+        const int cbi = t % CB;
+        const int hh = (t / CB) & 3;
+        const int rr = ((t / CB) >> 2) & 3;
+        const int mt = (t / CB) >> 4;
+        esx[it] = s_x[min(16 * mt + 4 * hh + rr, M - 1)];
+        esw[it] = h2f(s1[16 * min(nb0 + cbi, nbt - 1) + cc]);
+    }
+
     v4i acc[MT][CB];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -213,17 +233,17 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         else run(std::false_type{});
     }
 
-    // Sum the KW partial accumulators in LDS, then the epilogue. Output
-    // element (mt, r, h, cb, c) is token 16mt + 4h + r, channel
-    // 16(nb0 + cb) + c; consecutive threads take consecutive channels.
+    // Sum the KW partial accumulators in LDS, then the epilogue.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) red[((wave * MT + mt) * CB + cb) * 64 + lane] = acc[mt][cb];
     __syncthreads();
     const int* redi = reinterpret_cast<const int*>(red);
-    constexpr int E = MT * 16 * CB * 16;
-    for (int e = threadIdx.x; e < E; e += 64 * KW) {
+#pragma unroll
+    for (int it = 0; it < EI; ++it) {
+        const int e = int(threadIdx.x) + it * 64 * KW;
+        if (e >= E) break;
         const int cc = e & 15;
         int t = e >> 4;
         const int cbi = t % CB;
@@ -240,7 +260,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         for (int w = 0; w < KW; ++w) sum += redi[(((w * MT + mt) * CB + cbi) * 64 + l) * 4 + rr];
         const int n = 16 * nbi + cc;
         if (acc_debug) acc_debug[int64_t(m) * N + n] = sum;
-        y[int64_t(m) * N + n] = epilogue_value(sum, s_x[m], h2f(s1[n]));
+        y[int64_t(m) * N + n] = epilogue_value(sum, esx[it], esw[it]);
     }
 }
 
@@ -719,6 +739,225 @@ __global__ void __launch_bounds__(256) gemm_generic_kernel(
     }
 }
 
+// Per-token INT8 codes of V fp16 activations (V/2 words, two per word),
+// V bytes in input order, with the activation quantizer's arithmetic: the
+// fp32 product with the token's inv = fp32(127/absmax), rounded half to even.
+//   * The product is formed as fma(x, inv, 0): one rounding of the exact
+//     product, as a plain fp32 multiply (a zero product may come out +0
+//     instead of -0; its code is 0 either way).
+//   * The quantizer's clamp to +-127 never acts here: |x| <= absmax gives
+//     |x * inv| <= 127 (1 + 2^-24), which rounds to at most 127. So the codes
+//     equal the quantizer's for every finite input.
+//   * Rounding adds 1.5 * 2^23: in [2^23, 2^24) the fp32 spacing is 1, the
+//     addition rounds to nearest even, and the low byte of the sum is the
+//     code in two's complement.
+template <int V>
+__device__ __forceinline__ void act_codes(const uint32_t (&w)[V / 2], float inv,
+                                          uint32_t (&out)[(V + 3) / 4]) {
+    uint32_t b[V];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const float p = __builtin_fmaf(h2f(uint16_t(hf ? w[i] >> 16 : w[i] & 0xffffu)), inv, 0.0f);
+            b[2 * i + hf] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
+        }
+    }
+    // gather low bytes: perm(b1, b0) = [b0 b1 0 0]; two of those -> 4 bytes
+    if constexpr (V == 2) {
+        out[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i)
+            out[i] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[4 * i + 3], b[4 * i + 2], 0x0c0c0400u),
+                                           __builtin_amdgcn_perm(b[4 * i + 1], b[4 * i], 0x0c0c0400u),
+                                           0x05040100u);
+    }
+}
+
+// Fused family (M <= 16): per-token activation quantization inside the GEMM.
+//
+// For a handful of tokens the activation quantizer is a separate launch of
+// almost no work; here every workgroup quantizes the tokens itself. The
+// split of work is the decode family's with one 16-row tile: a workgroup
+// owns one column block over all of K, its KW waves split K into ranges of
+// at most kFusedGroups groups, and every load of a wave (packed weights,
+// group records, fp16 activations) is issued up front.
+//   * Only the M real tokens are quantized, spread over all 64 lanes: per
+//     group, lane l takes V consecutive inputs, V * (l % (128/V)) onward, of
+//     token l / (128/V) + (V/2) t for each of T rounds (V = 2 for one token,
+//     4 for two, else 8; token rows past M repeat the last token).
+//   * Token absmax: per-lane partial maxima on the fp16 magnitude bits, a
+//     shuffle reduction over the lanes of a token, one LDS slot per (wave,
+//     token), then a max over the waves (exact in any order).
+//   * Codes go to a per-wave LDS area (groups x tokens x 128 bytes) and are
+//     read back in the A-operand lane order of v_mfma_i32_16x16x64_i8 (lane
+//     (c, h): token c, 16 bytes at 16h of each half-group).
+//   * The KW partial accumulators are summed in LDS and the epilogue uses
+//     s_x = absmax / 127 as the quantizer stores it: outputs equal the
+//     two-call path's bit for bit.
+template <int V, int T, int KW>
+__global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
+    const uint16_t* __restrict__ x, int M, int K,
+    const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
+    const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_debug) {
+    constexpr int GM = kFusedGroups;
+    constexpr int LPR = kGroup / V;           // lanes per token row
+    constexpr int RR = 64 / LPR;              // token rows per round
+    constexpr int ROWS = RR * T;              // token rows held (>= M)
+    static_assert(ROWS <= 16, "at most one 16-row tile");
+    __shared__ v4i red[KW * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t aq[KW][GM * ROWS * kGroup];
+    __shared__ uint32_t pmax[KW][ROWS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15;
+    const int h = lane >> 4;
+    const int ng = K >> 7;
+    const int nb = blockIdx.x;
+    const int gpw = (ng + KW - 1) / KW;           // <= GM (checked by the launch plan)
+    const int gb = min(ng, wave * gpw);
+    const int cnt = min(ng, gb + gpw) - gb;
+
+    const uint8_t* bptr = nib + int64_t(nb) * ng * kBlockBytes + lane * 16;
+    const uint8_t* rptr = rec + (int64_t(nb) * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    // the channel scale of this thread's epilogue element, fetched now
+    const float esw = h2f(s1[16 * nb + (threadIdx.x & 15)]);
+    const int qj = lane % LPR;                    // V-value chunk within the group
+    int qrow[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) qrow[t] = min(lane / LPR + RR * t, M - 1);
+
+    // Activations first, so the absmax waits only for them while the weights
+    // are still in flight. Loads are unconditional -- groups past the wave's
+    // range repeat its last group (cache hits, never used) -- so the
+    // compiler's waits count exactly the loads issued.
+    uint32_t xv[T][GM][V / 2];
+    uint4 qn[GM];
+    uint32_t rs[GM];
+#pragma unroll
+    for (int i = 0; i < GM; ++i) {
+        {
+            const int g = min(gb + i, ng - 1);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const uint16_t* src = x + int64_t(qrow[t]) * K + g * kGroup + V * qj;
+                if constexpr (V == 8) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(src);
+                    xv[t][i][0] = v.x; xv[t][i][1] = v.y; xv[t][i][2] = v.z; xv[t][i][3] = v.w;
+                } else if constexpr (V == 4) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(src);
+                    xv[t][i][0] = v.x; xv[t][i][1] = v.y;
+                } else {
+                    xv[t][i][0] = *reinterpret_cast<const uint32_t*>(src);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < GM; ++i) {
+        {
+            const int g = min(gb + i, ng - 1);
+            qn[i] = *reinterpret_cast<const uint4*>(bptr + int64_t(g) * kBlockBytes);
+            rs[i] = *reinterpret_cast<const uint16_t*>(
+                rptr + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+        }
+    }
+    // token absmax on the magnitude bits (for finite fp16 their order is
+    // |x|'s), two 16-bit lanes at a time
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        us2 m2 = us2{0, 0};
+#pragma unroll
+        for (int i = 0; i < GM; ++i) {
+            if (i < cnt) {
+#pragma unroll
+                for (int j = 0; j < V / 2; ++j)
+                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, xv[t][i][j] & 0x7fff7fffu));
+            }
+        }
+        uint32_t mb = max(uint32_t(m2[0]), uint32_t(m2[1]));
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1)
+            mb = max(mb, uint32_t(__shfl_xor(int(mb), off, LPR)));
+        // lanes past M hold the last token: same maximum, same slot
+        if (qj == 0) pmax[wave][qrow[t]] = mb;
+    }
+    __syncthreads();
+    float inv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        uint32_t mm = 0;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) mm = max(mm, pmax[w][qrow[t]]);
+        const float a = h2f(uint16_t(mm));
+        inv[t] = a > 0.0f ? float(kActMax) / a : 0.0f;
+    }
+
+    // quantize the wave's whole K range into its LDS area, then read it back
+    // in operand order (written by other lanes of this wave: order the wave's
+    // LDS accesses; DS instructions of one wave complete in order)
+    uint8_t* my = aq[wave];
+#pragma unroll
+    for (int i = 0; i < GM; ++i) {
+        if (i < cnt) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                uint32_t code[(V + 3) / 4];
+                act_codes<V>(xv[t][i], inv[t], code);
+                uint8_t* dst = my + (i * ROWS + qrow[t]) * kGroup + V * qj;
+                if constexpr (V == 8) *reinterpret_cast<uint2*>(dst) = uint2{code[0], code[1]};
+                else if constexpr (V == 4) *reinterpret_cast<uint32_t*>(dst) = code[0];
+                else *reinterpret_cast<uint16_t*>(dst) = uint16_t(code[0]);
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int arow = min(c, M - 1);
+    v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < GM; ++i) {
+        if (i < cnt) {
+            const uint8_t* src = my + (i * ROWS + arow) * kGroup + 16 * h;
+            const v4i a0 = *reinterpret_cast<const v4i*>(src);
+            const v4i a1 = *reinterpret_cast<const v4i*>(src + 64);
+            v4i b0, b1;
+            dequant_block(qn[i], rs[i], b0, b1);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+        }
+    }
+
+    // sum the KW partial accumulators in LDS, then the epilogue (token
+    // 4h + r, channel 16 nb + c for lane (c, h), register r)
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    const int* redi = reinterpret_cast<const int*>(red);
+    for (int e = threadIdx.x; e < 256; e += 64 * KW) {
+        const int cc = e & 15;
+        const int hh = (e >> 4) & 3;
+        const int rr = e >> 6;
+        const int m = 4 * hh + rr;
+        if (m >= M) continue;
+        const int l = cc + 16 * hh;
+        int32_t sum = 0;
+        uint32_t mm = 0;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+            sum += redi[(w * 64 + l) * 4 + rr];
+            mm = max(mm, pmax[w][m]);
+        }
+        const float am = h2f(uint16_t(mm));
+        const float sx = am > 0.0f ? am / float(kActMax) : 0.0f;
+        const int n = 16 * nb + cc;
+        if (acc_debug) acc_debug[int64_t(m) * N + n] = sum;
+        y[int64_t(m) * N + n] = epilogue_value(sum, sx, esw);
+    }
+}
+
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 struct Args {
@@ -925,6 +1164,97 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
         case 1: return launch_generic<1, 2>(p, a, stream);
         case 2: return launch_generic<2, 2>(p, a, stream);
         default: return launch_generic<4, 2>(p, a, stream);
+    }
+}
+
+// Fused entry point: one launch of the fused family when M <= 8 and each
+// wave's K range fits kFusedGroups groups (K <= 8192 with 16 waves); other
+// shapes run the quantizer into the workspace, then the GEMM. (The fused
+// kernel takes up to 16 tokens when forced.)
+// QOQ_GEMM_CONFIG="fused,KW" forces the fused kernel with KW waves; any other
+// family forces the two-call path with that GEMM configuration.
+LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
+    LinearPlan p{};
+    p.valid = true;
+    const int64_t ng = K / kGroup;
+    const bool fits = M <= 16 && N * K / 2 < (int64_t(1) << 31) &&
+                      M * K * 2 < (int64_t(1) << 31) && ng <= int64_t(kFusedGroups) * 16;
+    // by default only up to 8 tokens: beyond that the workgroups' repeated
+    // quantization costs more than the separate quantizer launch saves
+    const bool pays = M <= 8;
+    int kw = ng <= 4 * kFusedGroups ? 4 : (ng <= 8 * kFusedGroups ? 8 : 16);
+    bool fused = fits && pays;
+    if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
+        if (env[0] != '\0') {
+            int a = 0;
+            char fam[16] = {0};
+            const int nf = std::sscanf(env, "%15[a-z0-9],%d", fam, &a);
+            if (std::string(fam) == "fused") {
+                fused = true;
+                kw = a;
+                if (nf != 2 || !fits || (a != 4 && a != 8 && a != 16) ||
+                    ng > int64_t(kFusedGroups) * a) {
+                    p.valid = false;
+                    return p;
+                }
+            } else {
+                fused = false;
+            }
+        }
+    }
+    if (fused) {
+        p.fused = true;
+        p.kw = kw;
+        p.grid_x = int(N / kBlockCols);
+        p.ws_bytes = 0;
+        return p;
+    }
+    p.fused = false;
+    p.gemm = plan_gemm(M, N, K);
+    if (p.gemm.kind < 0) {
+        p.valid = false;
+        return p;
+    }
+    p.x8_offset = 0;
+    p.sx_offset = round_up(act_bytes(M, K), 256);
+    p.gemm_ws_offset = round_up(p.sx_offset + 4 * M, 256);
+    p.ws_bytes = p.gemm_ws_offset + p.gemm.ws_bytes;
+    return p;
+}
+
+template <int V, int T>
+hipError_t launch_fused_vt(const LinearPlan& p, const uint16_t* x, int M, int K, const uint8_t* nib,
+                           const uint8_t* rec, int ng8, const uint16_t* s1, int N, uint16_t* y,
+                           int32_t* acc_debug, hipStream_t stream) {
+    switch (p.kw) {
+        case 4:
+            return launch_kernel(gemm_fused_small_kernel<V, T, 4>, dim3(p.grid_x), dim3(256), 0,
+                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
+        case 8:
+            return launch_kernel(gemm_fused_small_kernel<V, T, 8>, dim3(p.grid_x), dim3(512), 0,
+                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
+        case 16:
+            return launch_kernel(gemm_fused_small_kernel<V, T, 16>, dim3(p.grid_x), dim3(1024), 0,
+                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
+        default:
+            return hipErrorInvalidConfiguration;
+    }
+}
+
+hipError_t launch_linear_fused(const LinearPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
+                               int32_t* acc_debug, hipStream_t stream) {
+    const PackedLayout L = packed_layout(N, K);
+    const uint8_t* rec = packed + L.rec_offset;
+    const int m = int(M), k = int(K), n = int(N), ng8 = int(L.ng8);
+    if (m == 1) return launch_fused_vt<2, 1>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+    if (m == 2) return launch_fused_vt<4, 1>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+    switch ((m + 3) / 4) {
+        case 1: return launch_fused_vt<8, 1>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+        case 2: return launch_fused_vt<8, 2>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+        case 3: return launch_fused_vt<8, 3>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+        case 4: return launch_fused_vt<8, 4>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
+        default: return hipErrorInvalidConfiguration;
     }
 }
 

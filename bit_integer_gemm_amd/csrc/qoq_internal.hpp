@@ -68,6 +68,7 @@ constexpr int kRecChunk = 8;
 constexpr int kRecChunkBytes = kBlockCols * kRecChunk * 2;  // 256
 constexpr int kProtect = 119;   // level-1 protective range
 constexpr int kActMax = 127;    // activation code bound
+constexpr int kFusedGroups = 4;  // fused kernel: groups of K held per wave
 constexpr int kActTileRows = 16;
 constexpr int kActUnit = 256;                          // 16 rows x 16 bytes
 constexpr int kActGroupBytes = kActUnit * kGroup / 16; // 2048: one group of a row tile
@@ -121,6 +122,21 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
+// Launch plan of the fused entry point (activation quantization + GEMM):
+// either one fused launch (small M) or the quantizer into a workspace
+// followed by the GEMM.
+struct LinearPlan {
+    bool valid;         // false: QOQ_GEMM_CONFIG names no usable configuration
+    bool fused;
+    int kw;             // fused: waves splitting K
+    int grid_x;
+    int64_t x8_offset, sx_offset, gemm_ws_offset;   // workspace carve-up (two-call path)
+    int64_t ws_bytes;
+    GemmPlan gemm;      // two-call path
+};
+
+LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
+
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed, uint16_t* s1,
                        uint8_t* cq4, int8_t* cs2, uint8_t* cz, bool from_canonical,
@@ -130,5 +146,8 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm(const GemmPlan& plan, const int8_t* x8, const float* s_x, int64_t M,
                        int64_t K, const uint8_t* packed, const uint16_t* s1, int64_t N,
                        uint16_t* y, int32_t* acc_debug, void* workspace, hipStream_t stream);
+hipError_t launch_linear_fused(const LinearPlan& plan, const uint16_t* x, int64_t M, int64_t K,
+                               const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
+                               int32_t* acc_debug, hipStream_t stream);
 
 }  // namespace qoq

@@ -173,6 +173,37 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
                          uint16_t* y, int32_t* acc_debug,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes qoq_w4a8_linear needs for this shape: 0 when it runs as
+ * one fused launch (M <= 8 and K <= 8192), otherwise room for the x8 codes,
+ * the token scales and the GEMM's own workspace. No zero-fill is needed.
+ * Host-only. */
+size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Per-token activation quantization and W4A8 GEMM in one call (run time).
+ * Same result as qoq_quantize_act followed by qoq_w4a8_gemm, bit for bit
+ * (codes, accumulators and y). For M <= 8 and K <= 8192 a single kernel
+ * does both: every workgroup quantizes the few tokens itself, which removes
+ * a launch of almost no work from the decode step (pages: velog notes on
+ * QServe, "Methods / 2) System: QServe", and "Part5 LLM部署技术" section 3,
+ * on fusing the CUDA-core work into the GEMM). Other shapes run the
+ * quantizer into `workspace`, then the GEMM.
+ *   x            [M,K] fp16 bits, row-major, 16-byte aligned.
+ *   M >= 0, K > 0, K % 128 == 0, N > 0, N % 16 == 0, group == 128.
+ *   packed, s1   from qoq_pack_weights for the same N, K.
+ *   y            out [M,N] fp16 bits.   acc_debug  NULL or out [M,N] int32.
+ *   workspace    qoq_linear_workspace_bytes(M, N, K) bytes, 16-byte aligned
+ *                (may be NULL when that is 0); overlapping calls must not
+ *                share it.
+ * QOQ_GEMM_CONFIG="fused,KW" (KW in 4, 8, 16) forces the fused kernel
+ * (M <= 16, K <= 512 KW);
+ * any other family forces the two-call path with that GEMM configuration.
+ * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
+ * QOQ_ERR_WORKSPACE, QOQ_ERR_CONFIG, QOQ_ERR_HIP. */
+qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K,
+                           const void* packed, const uint16_t* s1, int64_t N, int32_t group,
+                           uint16_t* y, int32_t* acc_debug,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* qoq_status_string(int status);
 

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) >= {"qoq_pack_weights", "qoq_quantize_act", "qoq_w4a8_gemm",
                           "qoq_packed_weight_bytes", "qoq_gemm_workspace_bytes",
-                          "qoq_act_bytes", "qoq_status_string"}
+                          "qoq_act_bytes", "qoq_status_string", "qoq_w4a8_linear",
+                          "qoq_linear_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -141,6 +142,52 @@ def test_gemm_rejects_bad_arguments():
         assert call(M=M, workspace=None, workspace_bytes=need) == WORKSPACE
         assert call(M=M, workspace=P, workspace_bytes=need - 1) == WORKSPACE
         assert call(M=M, workspace=P + 4, workspace_bytes=need) == ALIGN
+
+
+def test_linear_workspace_bytes():
+    # one fused launch for M <= 8 and K <= 8192: no workspace
+    for M, K in [(1, 4096), (8, 8192), (8, 128)]:
+        assert qoq.qoq_linear_workspace_bytes(M, 4096, K) == 0
+    # otherwise x8 (tile layout) + token scales, each 256-byte aligned
+    for M, K in [(9, 4096), (16, 128), (64, 4096), (8, 14336), (4096, 4096)]:
+        act = qoq.qoq_act_bytes(M, K)
+        want = -(-act // 256) * 256 + -(-4 * M // 256) * 256
+        assert qoq.qoq_linear_workspace_bytes(M, 4096, K) == want
+    assert qoq.qoq_linear_workspace_bytes(0, 4096, 4096) == 0
+    assert qoq.qoq_linear_workspace_bytes(4, 4000, 4096) == 0
+
+
+def test_linear_rejects_bad_arguments(monkeypatch):
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    f = qoq.qoq_w4a8_linear
+    args = dict(x=P, M=4, K=4096, packed=P, s1=P, N=4096, group=128, y=P,
+                acc_debug=None, workspace=None, workspace_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(group=64) == GROUP
+    assert call(K=4000) == SHAPE
+    assert call(N=4008) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(M=0) == OK
+    for name in ("x", "packed", "s1", "y"):
+        assert call(**{name: None}) == NULL, name
+    assert call(x=P + 2) == ALIGN
+    assert call(y=P + 2) == ALIGN
+    need = qoq.qoq_linear_workspace_bytes(64, 4096, 4096)
+    assert need > 0
+    assert call(M=64) == WORKSPACE
+    assert call(M=64, workspace=P, workspace_bytes=need - 1) == WORKSPACE
+    assert call(M=64, workspace=P + 8, workspace_bytes=need) == ALIGN
+    # the fused kernel cannot take 64 tokens: a forced fused configuration is refused
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,8")
+    assert call(M=64, workspace=P, workspace_bytes=need) == 8
+    assert call(M=4, K=16384) == 8          # 128 groups do not fit 8 waves x 4 groups
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,5")
+    assert call() == 8
 
 
 def test_binding_refuses_cpu_tensors():

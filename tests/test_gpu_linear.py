@@ -1,0 +1,89 @@
+"""The one-call entry point (activation quantization + W4A8 GEMM) against
+the oracle and against the two-call path.
+
+Small M runs the fused kernel, which quantizes the tokens inside the GEMM;
+its codes, accumulators and fp16 outputs must equal the two-call path's bit
+for bit, and the accumulators the oracle's. Larger shapes run the two-call
+path through the workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+qoq = pytest.importorskip("bit_integer_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# (M, K, N): one to sixteen tokens, group counts that do and do not fill the
+# waves, column counts that fill no tile
+FUSED = [(1, 128, 16), (1, 4096, 4096), (5, 640, 208), (8, 1152, 400), (8, 8192, 528),
+         (3, 2048, 1040), (4, 512, 512), (2, 384, 48)]
+# (the fused kernel also takes up to 16 tokens when forced)
+FORCED = FUSED + [(16, 8192, 528), (13, 2048, 1040), (9, 512, 512), (12, 640, 16)]
+TWO_CALL = [(17, 1024, 208), (64, 4096, 4096), (8, 14336, 272), (100, 640, 400), (16, 512, 512)]
+
+
+def _half(X):
+    return torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV)
+
+
+def _check(M, K, N, monkeypatch, cfg=None):
+    W, X, _ = wl.make_inputs(M, K, N, seed=7 * M + K + N)
+    pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
+    xd = _half(X)
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    x8, s_x = qoq.quantize_act(xd)
+    y2, acc2 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    if cfg is not None:
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+    print(f"\n[gpu-case] linear cfg={cfg} M={M} K={K} N={N}", flush=True)
+    y1, acc1 = qoq.w4a8_linear(xd, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    ref = oracle.w4a8_linear(X, W)
+    assert np.array_equal(acc1.cpu().numpy().astype(np.int64), ref["acc"]), "acc vs oracle"
+    assert torch.equal(acc1, acc2), "acc vs two-call path"
+    assert torch.equal(y1, y2), "y vs two-call path"
+    yy = y1.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3, f"max rel err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("M,K,N", FUSED)
+def test_fused_default(M, K, N, monkeypatch):
+    assert qoq.qoq_linear_workspace_bytes(M, N, K) == 0
+    _check(M, K, N, monkeypatch)
+
+
+@pytest.mark.parametrize("kw", [4, 8, 16])
+def test_fused_every_wave_count(kw, monkeypatch):
+    for (M, K, N) in FORCED:
+        if K // 128 <= 4 * kw:
+            _check(M, K, N, monkeypatch, cfg=f"fused,{kw}")
+
+
+@pytest.mark.parametrize("M,K,N", TWO_CALL)
+def test_two_call_path(M, K, N, monkeypatch):
+    assert qoq.qoq_linear_workspace_bytes(M, N, K) > 0
+    _check(M, K, N, monkeypatch)
+
+
+def test_forced_two_call_path_for_small_m(monkeypatch):
+    _check(8, 1152, 400, monkeypatch, cfg="decode,1,1,8,4")
+
+
+def test_zero_rows_and_empty_batch(monkeypatch):
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    W, X, _ = wl.make_inputs(6, 1024, 96, seed=3)
+    X[2] = 0
+    X[5] = 0
+    pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
+    y, acc = qoq.w4a8_linear(_half(X), pw, acc_debug=True)
+    ref = oracle.w4a8_linear(X, W)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    assert torch.all(y[2] == 0) and torch.all(y[5] == 0)
+    y0 = qoq.w4a8_linear(torch.empty((0, 1024), dtype=torch.float16, device=DEV), pw)
+    assert y0.shape == (0, 96)

@@ -462,17 +462,22 @@ __device__ __forceinline__ void tile_of(int L, int tiles_m, int tiles_n, int& tm
 //     rings) so two workgroups share a CU: one's barrier waits, LDS latency
 //     and dequantization bursts are covered by the other's MFMAs.
 //   * Epilogue through LDS with 16-byte row-segment stores.
-template <int MT, int CB, int PB, int MINB>
-__global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
+template <int MT, int CB, int PB, int MINB, int NW>
+__global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
     const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
     int32_t* __restrict__ acc_debug) {
     constexpr int AF = 4 * MT;                    // A fragments per group
-    constexpr int AFW = AF / 4;                   // fetched per wave (= MT)
+    constexpr int AFW = (AF + NW - 1) / NW;       // fetched per wave
     static_assert(AF * 2 <= 64, "LDS slots above 64 KiB");
-    static_assert(PB >= 1 && PB <= 4, "weight ring depth");
-    __shared__ v4i As[2][AF][64];
+    static_assert(PB == 1 || PB == 2 || PB == 4 || PB == 8, "weight ring depth divides 8");
+    // two slots of A fragments; the epilogue reuses the space to stage NW
+    // blocks of 32 x 32CB fp16 outputs
+    constexpr int kSlotsBytes = 2 * AF * 64 * 16;
+    constexpr int kStageBytes = NW * 32 * 32 * CB * 2;
+    __shared__ v4i lds_raw[(kSlotsBytes > kStageBytes ? kSlotsBytes : kStageBytes) / 16];
+    v4i (*As)[AF][64] = reinterpret_cast<v4i (*)[AF][64]>(lds_raw);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31;
@@ -480,7 +485,7 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
     const int c = lane & 15;
     const int ng = K >> 7;
     const int nbt = N >> 4;
-    constexpr int BM = 32 * MT, BNB = 8 * CB;    // tile rows, tile 16-column blocks
+    constexpr int BM = 32 * MT, BNB = 2 * CB * NW;   // tile rows, tile 16-column blocks
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (nbt + BNB - 1) / BNB;
     int tm, tn;
@@ -494,14 +499,19 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
         (void*)nib, (short)0, nbt * ng * kBlockBytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)rec, (short)0, nbt * ng8 * (kBlockCols * kRecChunk * 2), 0x00020000);
-    // A fragment (32-row tile u, step st) of group g: lanes 0-31 take rows
-    // 0-31 of the tile at inputs 32st .. +15, lanes 32-63 the next 16 inputs;
-    // in the tile layout that is two 512-byte runs. Rows at or beyond M read
-    // the last row (never stored).
-    int a_lane[AFW];
+    // A fragment f = (32-row tile f / 4, step f % 4) of group g: lanes 0-31
+    // take rows 0-31 of the tile at inputs 32 (f % 4) .. +15, lanes 32-63 the
+    // next 16 inputs; in the tile layout that is two 512-byte runs. Wave w
+    // fetches and stages fragments w, w + NW, ... Rows at or beyond M read the
+    // last row (never stored).
+    int a_lane[AFW], a_soff[AFW];
 #pragma unroll
-    for (int u = 0; u < AFW; ++u)
-        a_lane[u] = int(act_row_offset(min(m0 + 32 * u + j, M - 1), K)) + kActUnit * q;
+    for (int u = 0; u < AFW; ++u) {
+        const int f = min(wave + NW * u, AF - 1);
+        a_lane[u] = int(act_row_offset(min(m0 + 32 * (f >> 2) + j, M - 1), K)) + kActUnit * q;
+        a_soff[u] = 2 * kActUnit * (f & 3);
+    }
+    auto owns = [&](int u) { return wave + NW * u < AF; };
     int b_lane[CB], r_lane[CB];
 #pragma unroll
     for (int t = 0; t < CB; ++t) {
@@ -535,14 +545,14 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
         g = min(g, ng - 1);
 #pragma unroll
         for (int u = 0; u < AFW; ++u) {
-            // fragment f = wave + 4u: row tile u, step wave
-            const int soff = g * kActGroupBytes + 2 * kActUnit * wave;
+            const int soff = g * kActGroupBytes + a_soff[u];
             ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane[u], soff, 0));
         }
     };
     auto stage_a = [&](int slot) {
 #pragma unroll
-        for (int u = 0; u < AFW; ++u) As[slot][wave + 4 * u][lane] = ar[u];
+        for (int u = 0; u < AFW; ++u)
+            if (owns(u)) As[slot][wave + NW * u][lane] = ar[u];
     };
     auto load_b = [&](int p, int g) {
         g = min(g, ng - 1);
@@ -611,9 +621,8 @@ __global__ void __launch_bounds__(256, MINB) gemm_tile32_kernel(
     // block to fp16 into a staging area (reusing the A slots), then writes it
     // out as 16-byte row segments. Lane (j, q), register r of tile (mt, t)
     // holds row 32mt + 8(r/4) + 4q + r%4, column 32t + j of the wave's columns.
-    static_assert(4 * 32 * 32 * CB * 2 <= int(sizeof(As)), "staging does not fit the A slots");
     __syncthreads();
-    uint16_t* stage = reinterpret_cast<uint16_t*>(&As[0][0][0]) + wave * (32 * 32 * CB);
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw) + wave * (32 * 32 * CB);
     const int n0w = 16 * nbw;
     float sw[CB];
 #pragma unroll
@@ -987,10 +996,11 @@ hipError_t launch_lds(const GemmPlan& p, const Args& a, hipStream_t stream) {
                          a.acc_debug);
 }
 
-template <int MT, int CB, int PB, int MINB>
+template <int MT, int CB, int PB, int MINB, int NW>
 hipError_t launch_tile32(const GemmPlan& p, const Args& a, hipStream_t stream) {
-    return launch_kernel(gemm_tile32_kernel<MT, CB, PB, MINB>, dim3(p.grid_x), dim3(256), 0, stream,
-                         a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y, a.acc_debug);
+    return launch_kernel(gemm_tile32_kernel<MT, CB, PB, MINB, NW>, dim3(p.grid_x), dim3(64 * NW), 0,
+                         stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+                         a.acc_debug);
 }
 
 template <int MT, int CB>
@@ -1027,13 +1037,19 @@ bool lds_config_exists(int mt, int cb, int nw, int pp) {
     return false;
 }
 
-// Every compiled 32x32 tile configuration: (MT, CB, PB, workgroups per CU).
+// Every compiled 32x32 tile configuration: (MT, CB, PB, workgroups per CU,
+// waves per workgroup).
 #define QOQ_TILE32_CONFIGS(X)                                                        \
-    X(4, 2, 2, 2) X(4, 2, 1, 2) X(4, 1, 2, 2) X(2, 2, 2, 2) X(2, 1, 2, 2) X(8, 1, 1, 2)  \
-    X(4, 2, 2, 1) X(8, 1, 2, 1) X(8, 2, 2, 1) X(2, 1, 2, 3) X(4, 1, 2, 3)
+    X(4, 2, 2, 2, 4) X(4, 2, 1, 2, 4) X(4, 1, 2, 2, 4) X(2, 2, 2, 2, 4) X(2, 1, 2, 2, 4)   \
+    X(8, 1, 1, 2, 4) X(4, 2, 2, 1, 4) X(8, 1, 2, 1, 4) X(8, 2, 2, 1, 4) X(2, 1, 2, 3, 4)   \
+    X(4, 1, 2, 3, 4) X(2, 1, 4, 2, 4) X(2, 1, 8, 2, 4) X(2, 2, 4, 2, 4) X(2, 1, 4, 3, 4)   \
+    X(2, 1, 8, 1, 4) X(2, 2, 8, 1, 4) X(4, 1, 4, 2, 4) X(1, 1, 4, 3, 4) X(1, 1, 2, 3, 4)   \
+    X(1, 1, 8, 2, 4) X(1, 1, 4, 4, 4) X(2, 1, 4, 1, 6) X(2, 1, 2, 1, 6) X(2, 1, 4, 1, 8)   \
+    X(2, 1, 2, 1, 8) X(2, 1, 4, 1, 3) X(2, 1, 4, 2, 3) X(1, 1, 4, 1, 6) X(2, 1, 8, 1, 6)   \
+    X(4, 1, 2, 1, 8) X(4, 2, 2, 1, 8)
 
-bool tile32_config_exists(int mt, int cb, int pb, int minb) {
-#define X(a, b, c, d) if (mt == a && cb == b && pb == c && minb == d) return true;
+bool tile32_config_exists(int mt, int cb, int pb, int minb, int nw) {
+#define X(a, b, c, d, e) if (mt == a && cb == b && pb == c && minb == d && nw == e) return true;
     QOQ_TILE32_CONFIGS(X)
 #undef X
     return false;
@@ -1056,8 +1072,10 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 //                        workgroup, one or two column blocks per workgroup;
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
 //                        LDS, waves side by side along N;
-//   M  > 64:             32x32 tile family, tile size picked so that at
-//                        least ~2 workgroups per CU exist.
+//   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
+//                        they fill whole rounds of the CUs, 128 x 256 tiles of
+//                        8 waves for short, deep shapes (N <= 8192), else
+//                        4-wave tiles sized so that ~2 workgroups per CU exist.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p{};
     const int64_t nbt = N / kBlockCols;
@@ -1089,25 +1107,33 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     } else {
         p.kind = 4;
         p.pa = 2;   // workgroups per CU
-        const int64_t t42 = ((M + 127) / 128) * ((nbt + 15) / 16);
+        p.nw = 4;
+        const int64_t rows128 = (M + 127) / 128;
+        const int64_t t42 = rows128 * ((nbt + 15) / 16);       // 128 x 256 tiles
         const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
-        if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
+        const int64_t t_wide = rows128 * ((nbt + 31) / 32);    // 128 x 512 tiles, 8 waves
+        // whole rounds of one wide tile per CU: the tail round is >= 90 % full
+        const bool wide_fills = t_wide >= 512 && (t_wide % 256 == 0 || t_wide % 256 >= 230);
+        if (wide_fills) { p.mt = 4; p.cb = 2; p.pd = 2; p.pa = 1; p.nw = 8; }
+        else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
+        else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
         else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
-        else { p.mt = 2; p.cb = 1; p.pd = 2; }
+        else { p.mt = 2; p.cb = 1; p.pd = 4; }
     }
     if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
         if (env[0] != '\0') {
-            int a = 0, b = 0, c = 0, d = 0;
+            int a = 0, b = 0, c = 0, d = 0, e = 4;
             char fam[16] = {0};
-            const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d", fam, &a, &b, &c, &d);
+            const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d,%d", fam, &a, &b, &c, &d, &e);
             const std::string f(fam);
             p.kind = -1;   // an override that names no compiled configuration is an error
             if (f == "decode" && nf == 5 && M <= 16 * a && decode_config_exists(a, b, c, d)) {
                 p.kind = 1; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
             } else if (f == "lds" && nf == 5 && lds_config_exists(a, b, c, d)) {
                 p.kind = 2; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
-            } else if (f == "tile32" && nf == 5 && small_offsets && tile32_config_exists(a, b, c, d)) {
-                p.kind = 4; p.mt = a; p.cb = b; p.pd = c; p.pa = d;
+            } else if (f == "tile32" && (nf == 5 || nf == 6) && small_offsets &&
+                       tile32_config_exists(a, b, c, d, e)) {
+                p.kind = 4; p.mt = a; p.cb = b; p.pd = c; p.pa = d; p.nw = e;
             } else if (f == "generic" && nf >= 3 && (a == 1 || a == 2 || a == 4) && b == 2) {
                 p.kind = 0; p.mt = a; p.cb = b;
             }
@@ -1119,7 +1145,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.grid_y = 1;
     } else if (p.kind == 4) {
         const int64_t tm = (M + 32 * p.mt - 1) / (32 * p.mt);
-        const int64_t tn = (nbt + 8 * p.cb - 1) / (8 * p.cb);
+        const int64_t tn = (nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw);
         p.grid_x = int(tm * tn);
         p.grid_y = 1;
     } else if (p.kind == 2) {
@@ -1147,8 +1173,9 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
         return hipErrorInvalidConfiguration;
     }
     if (p.kind == 4) {
-#define X(A, B, C, D) \
-    if (p.mt == A && p.cb == B && p.pd == C && p.pa == D) return launch_tile32<A, B, C, D>(p, a, stream);
+#define X(A, B, C, D, E)                                                              \
+    if (p.mt == A && p.cb == B && p.pd == C && p.pa == D && p.nw == E)                    \
+        return launch_tile32<A, B, C, D, E>(p, a, stream);
         QOQ_TILE32_CONFIGS(X)
 #undef X
         return hipErrorInvalidConfiguration;

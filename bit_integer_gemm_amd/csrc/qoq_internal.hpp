@@ -113,6 +113,7 @@ struct GemmPlan {
     int kw;             // decode: waves splitting K; shared-activation: waves per workgroup
     int pd;             // weight groups kept in flight per wave (register ring depth)
     int pa;             // 32x32 tile: workgroups per CU the kernel is built for
+    int nw;             // 32x32 tile: waves per workgroup (side by side along N)
     int grid_x, grid_y, splits;
     int groups_per_split;
     int64_t ws_acc_bytes;   // int32 partial sums

@@ -162,7 +162,7 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * M == 0 launches nothing.
  * Kernel choice: the library picks a kernel family and tile from (M, N, K).
  * The environment variable QOQ_GEMM_CONFIG ("decode,MT,CB,KW,PD",
- * "lds,MT,CB,NW,PD", "tile32,MT,CB,PB,WGPERCU" or "generic,MT,2") forces one
+ * "lds,MT,CB,NW,PD", "tile32,MT,CB,PB,WGPERCU[,NW]" or "generic,MT,2") forces one
  * compiled configuration for measurements; every configuration computes the
  * same INT32 accumulators. A value naming no compiled configuration valid
  * for the shape makes the call fail with QOQ_ERR_CONFIG (nothing launched).

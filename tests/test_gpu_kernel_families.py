@@ -31,8 +31,13 @@ LDS = [(1, 1, 4, 2), (1, 2, 4, 2), (1, 1, 8, 2), (1, 2, 8, 2), (1, 4, 4, 2), (2,
        (4, 1, 6, 4), (4, 2, 6, 4), (4, 1, 12, 4), (4, 1, 12, 2), (4, 1, 16, 2), (1, 1, 6, 4),
        (1, 1, 12, 4), (2, 1, 6, 4), (2, 1, 12, 4), (4, 1, 12, 8), (4, 1, 8, 8), (4, 1, 6, 8),
        (4, 2, 6, 8), (4, 1, 4, 8)]
-TILE32 = [(4, 2, 2, 2), (4, 2, 1, 2), (4, 1, 2, 2), (2, 2, 2, 2), (2, 1, 2, 2), (8, 1, 1, 2),
-          (4, 2, 2, 1), (8, 1, 2, 1), (8, 2, 2, 1), (2, 1, 2, 3), (4, 1, 2, 3)]
+TILE32 = [(4, 2, 2, 2, 4), (4, 2, 1, 2, 4), (4, 1, 2, 2, 4), (2, 2, 2, 2, 4), (2, 1, 2, 2, 4),
+          (8, 1, 1, 2, 4), (4, 2, 2, 1, 4), (8, 1, 2, 1, 4), (8, 2, 2, 1, 4), (2, 1, 2, 3, 4),
+          (4, 1, 2, 3, 4), (2, 1, 4, 2, 4), (2, 1, 8, 2, 4), (2, 2, 4, 2, 4), (2, 1, 4, 3, 4),
+          (2, 1, 8, 1, 4), (2, 2, 8, 1, 4), (4, 1, 4, 2, 4), (1, 1, 4, 3, 4), (1, 1, 2, 3, 4),
+          (1, 1, 8, 2, 4), (1, 1, 4, 4, 4), (2, 1, 4, 1, 6), (2, 1, 2, 1, 6), (2, 1, 4, 1, 8),
+          (2, 1, 2, 1, 8), (2, 1, 4, 1, 3), (2, 1, 4, 2, 3), (1, 1, 4, 1, 6), (2, 1, 8, 1, 6),
+          (4, 1, 2, 1, 8), (4, 2, 2, 1, 8)]
 GENERIC = [(1, 2), (2, 2), (4, 2)]
 
 # (M, K, N): odd group counts, N not a multiple of any tile width

@@ -32,6 +32,7 @@ __all__ = [
     "qoq_linear_workspace_bytes",
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
     "Workspace", "empty_act", "w4a8_linear",
+    "w8a8_pack_weights", "w8a8_gemm", "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_gemm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -86,6 +87,23 @@ def lib() -> ctypes.CDLL:
         L.qoq_linear_workspace_bytes.restype = sz
         L.qoq_w4a8_linear.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.qoq_w4a8_linear.restype = ctypes.c_int
+        # comparison GEMMs (include/qoq_variants.h)
+        L.qoq_w8a8_weight_bytes.argtypes = [i64, i64]
+        L.qoq_w8a8_weight_bytes.restype = sz
+        L.qoq_w8a8_pack_weights.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.qoq_w8a8_pack_weights.restype = ctypes.c_int
+        L.qoq_w8a8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.qoq_w8a8_gemm.restype = ctypes.c_int
+        L.qoq_w4a4_weight_bytes.argtypes = [i64, i64]
+        L.qoq_w4a4_weight_bytes.restype = sz
+        L.qoq_w4a4_act_bytes.argtypes = [i64, i64]
+        L.qoq_w4a4_act_bytes.restype = sz
+        L.qoq_w4a4_pack_weights.argtypes = [vp, i64, i64, vp, vp]
+        L.qoq_w4a4_pack_weights.restype = ctypes.c_int
+        L.qoq_w4a4_quantize_act.argtypes = [vp, i64, i64, vp, vp]
+        L.qoq_w4a4_quantize_act.restype = ctypes.c_int
+        L.qoq_w4a4_gemm.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        L.qoq_w4a4_gemm.restype = ctypes.c_int
         L.qoq_status_string.argtypes = [ctypes.c_int]
         L.qoq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -322,3 +340,69 @@ def w4a8_linear(x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
                            w.group, y.data_ptr(), _ptr(acc), ws_ptr, ws_bytes, _stream(dev)),
            "qoq_w4a8_linear")
     return (y, acc) if acc_debug else y
+
+
+# ---------------------------------------------------------------------------
+# comparison GEMMs (W8A8 per-channel; W4A4 per-group with partial-sum scaling)
+# ---------------------------------------------------------------------------
+def w8a8_pack_weights(W: torch.Tensor):
+    """Per-channel INT8 weights of W fp32 [N, K] -> (packed uint8, s fp16 [N])."""
+    _need_gpu(W, "W", torch.float32)
+    N, K = W.shape
+    nbytes = int(lib().qoq_w8a8_weight_bytes(N, K))
+    if nbytes == 0:
+        raise QoQError(2, "qoq_w8a8_pack_weights")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    s = torch.empty(N, dtype=torch.float16, device=W.device)
+    _check(lib().qoq_w8a8_pack_weights(W.data_ptr(), N, K, packed.data_ptr(), s.data_ptr(),
+                                       _stream(W.device)), "qoq_w8a8_pack_weights")
+    return packed, s
+
+
+def w8a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s: torch.Tensor,
+              N: int, acc_debug: bool = False):
+    """W8A8 GEMM on x8/s_x from quantize_act: y fp16 [M, N] (and acc int32)."""
+    _need_gpu(s_x, "s_x", torch.float32)
+    M, K = s_x.shape[0], x8.shape[1] * 16
+    _check_act(x8, M, K)
+    dev = x8.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if acc_debug else None
+    _check(lib().qoq_w8a8_gemm(x8.data_ptr(), s_x.data_ptr(), M, K, packed.data_ptr(),
+                               s.data_ptr(), N, y.data_ptr(), _ptr(acc), _stream(dev)),
+           "qoq_w8a8_gemm")
+    return (y, acc) if acc_debug else y
+
+
+def w4a4_pack_weights(W: torch.Tensor) -> torch.Tensor:
+    """Per-(channel, group) INT4 weights of W fp32 [N, K] -> packed uint8."""
+    _need_gpu(W, "W", torch.float32)
+    N, K = W.shape
+    nbytes = int(lib().qoq_w4a4_weight_bytes(N, K))
+    if nbytes == 0:
+        raise QoQError(2, "qoq_w4a4_pack_weights")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    _check(lib().qoq_w4a4_pack_weights(W.data_ptr(), N, K, packed.data_ptr(), _stream(W.device)),
+           "qoq_w4a4_pack_weights")
+    return packed
+
+
+def w4a4_quantize_act(x: torch.Tensor) -> torch.Tensor:
+    """Per-(token, group) INT4 activations of x fp16 [M, K] -> act uint8
+    (x4 tile layout, then the fp32 group scales)."""
+    _need_gpu(x, "x", torch.float16)
+    M, K = x.shape
+    nbytes = int(lib().qoq_w4a4_act_bytes(M, K)) if M > 0 else 0
+    act = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().qoq_w4a4_quantize_act(x.data_ptr(), M, K, act.data_ptr(), _stream(x.device)),
+           "qoq_w4a4_quantize_act")
+    return act
+
+
+def w4a4_gemm(act: torch.Tensor, M: int, K: int, packed: torch.Tensor, N: int) -> torch.Tensor:
+    """W4A4 GEMM with per-group partial-sum scaling: y fp16 [M, N]."""
+    _need_gpu(act, "act", torch.uint8)
+    y = torch.empty((M, N), dtype=torch.float16, device=act.device)
+    _check(lib().qoq_w4a4_gemm(act.data_ptr(), M, K, packed.data_ptr(), N, y.data_ptr(),
+                               _stream(act.device)), "qoq_w4a4_gemm")
+    return y

@@ -2,6 +2,7 @@
 // launches on the caller's stream. Nothing here allocates, frees,
 // synchronizes or prints.
 #include "qoq.h"
+#include "qoq_variants.h"
 #include "qoq_internal.hpp"
 
 namespace {
@@ -140,6 +141,91 @@ qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const void* 
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
+size_t qoq_w8a8_weight_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K, qoq::kGroup) != QOQ_OK) return 0;
+    return size_t(N * K);
+}
+
+qoq_status qoq_w8a8_pack_weights(const float* W, int64_t N, int64_t K, void* packed, uint16_t* s,
+                                 void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (W == nullptr || packed == nullptr || s == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(W) || misaligned(packed)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_w8a8_pack(W, N, K, static_cast<uint8_t*>(packed), s,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_w8a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
+                         const void* packed, const uint16_t* s, int64_t N, uint16_t* y,
+                         int32_t* acc_debug, void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x8 == nullptr || s_x == nullptr || packed == nullptr || s == nullptr || y == nullptr)
+        return QOQ_ERR_NULL;
+    if (misaligned(x8) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
+    if (N * K >= (int64_t(1) << 31) || qoq::act_bytes(M, K) >= (int64_t(1) << 31))
+        return QOQ_ERR_SHAPE;
+    const qoq::VariantPlan plan = qoq::plan_variant(qoq::kVariantW8A8, M, N, K);
+    if (!plan.valid) return QOQ_ERR_CONFIG;
+    const hipError_t e = qoq::launch_w8a8_gemm(plan, x8, s_x, M, K,
+                                               static_cast<const uint8_t*>(packed), s, N, y,
+                                               acc_debug, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+size_t qoq_w4a4_weight_bytes(int64_t N, int64_t K) { return qoq_packed_weight_bytes(N, K, qoq::kGroup); }
+
+size_t qoq_w4a4_act_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || K % qoq::kGroup != 0 || M > kMaxDim || K > kMaxDim) return 0;
+    return size_t(qoq::w4a4_act_bytes(M, K));
+}
+
+qoq_status qoq_w4a4_pack_weights(const float* W, int64_t N, int64_t K, void* packed,
+                                 void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (W == nullptr || packed == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(W) || misaligned(packed)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_w4a4_pack(W, N, K, static_cast<uint8_t*>(packed),
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_w4a4_quantize_act(const uint16_t* x, int64_t M, int64_t K, void* act,
+                                 void* stream) {
+    if (M < 0 || K <= 0 || K % qoq::kGroup != 0 || M > kMaxDim || K > kMaxDim)
+        return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x == nullptr || act == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(x) || misaligned(act)) return QOQ_ERR_ALIGN;
+    if (qoq::w4a4_act_bytes(M, K) >= (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    const hipError_t e = qoq::launch_w4a4_quantize_act(x, M, K, static_cast<uint8_t*>(act),
+                                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_w4a4_gemm(const void* act, int64_t M, int64_t K, const void* packed, int64_t N,
+                         uint16_t* y, void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (act == nullptr || packed == nullptr || y == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(act) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
+    if (N * K / 2 >= (int64_t(1) << 31) || qoq::w4a4_act_bytes(M, K) >= (int64_t(1) << 31))
+        return QOQ_ERR_SHAPE;
+    const qoq::VariantPlan plan = qoq::plan_variant(qoq::kVariantW4A4, M, N, K);
+    if (!plan.valid) return QOQ_ERR_CONFIG;
+    const hipError_t e = qoq::launch_w4a4_gemm(plan, static_cast<const uint8_t*>(act), M, K,
+                                               static_cast<const uint8_t*>(packed), N, y,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
 const char* qoq_status_string(int status) {
     switch (status) {
         case QOQ_OK: return "ok";
@@ -150,7 +236,7 @@ const char* qoq_status_string(int status) {
         case QOQ_ERR_WORKSPACE: return "workspace missing or too small";
         case QOQ_ERR_HIP: return "HIP kernel launch failed";
         case QOQ_ERR_FLAGS: return "unknown flag bits";
-        case QOQ_ERR_CONFIG: return "QOQ_GEMM_CONFIG names no compiled kernel configuration for this shape";
+        case QOQ_ERR_CONFIG: return "QOQ_GEMM_CONFIG / QOQ_VARIANT_CONFIG names no compiled kernel configuration for this shape";
         default: return "unknown status";
     }
 }

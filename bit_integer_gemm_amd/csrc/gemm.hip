@@ -16,6 +16,7 @@
 //     and independent of tiling and of the split of K.
 // Epilogue: y = fp16(acc * (s_x[m] * s1[n])), once per output.
 #include "qoq_internal.hpp"
+#include "kernel_common.hpp"
 
 #include <hip/hip_fp16.h>
 
@@ -26,45 +27,6 @@
 
 namespace qoq {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-// Four UINT4 codes (one per byte) -> four INT8 weights, register-parallel.
-__device__ __forceinline__ int dequant4(uint32_t codes, uint32_t mul2, uint32_t add2) {
-    const us2 r = __builtin_bit_cast(us2, codes) * __builtin_bit_cast(us2, mul2) +
-                  __builtin_bit_cast(us2, add2);
-    return int(__builtin_bit_cast(uint32_t, r) ^ 0x80808080u);
-}
-
-__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
-
-__device__ __forceinline__ uint16_t epilogue_value(int32_t acc, float sx, float sw) {
-    const float v = float(acc) * (sx * sw);
-    return __half_as_ushort(__float2half_rn(v));
-}
-
-// One lane's 16 packed bytes (32 codes of one channel) -> the B operands of
-// the two MFMA steps of the group: low nibbles -> step 0, high -> step 1.
-// `rec` holds s2 in bits 0-7 and 128 - z*s2 in bits 8-15.
-__device__ __forceinline__ void dequant_block(const uint4 q, uint32_t rec, v4i& b0, v4i& b1) {
-    // byte permutes: s2 into both 16-bit halves, the bias into all four bytes
-    const uint32_t mul2 = __builtin_amdgcn_perm(0u, rec, 0x0c000c00u);
-    const uint32_t add2 = __builtin_amdgcn_perm(0u, rec, 0x01010101u);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        b0[i] = dequant4(w[i] & 0x0F0F0F0Fu, mul2, add2);
-        b1[i] = dequant4((w[i] >> 4) & 0x0F0F0F0Fu, mul2, add2);
-    }
-}
-
-// Record of group (8j + u) from the 16-byte chunk of groups 8j..8j+7 (u static).
-__device__ __forceinline__ uint32_t record_of(const uint4 chunk, int u) {
-    const uint32_t w[4] = {chunk.x, chunk.y, chunk.z, chunk.w};
-    return (w[u >> 1] >> (16 * (u & 1))) & 0xffffu;
-}
 
 // Decode family (M <= 64): weight streaming.
 //
@@ -419,25 +381,6 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
                 y[int64_t(m) * N + n] = epilogue_value(v, s_x[m], sw);
             }
     }
-}
-
-// Tiles are assigned XCD-aware: the workgroups that land on one XCD (ids
-// congruent mod 8, the hardware's round-robin dispatch) take a contiguous run
-// of tiles in grouped order (8 tile rows at a time), so each XCD's L2 sees a
-// compact block of activation rows and weight columns.
-__device__ __forceinline__ void tile_of(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int T = tiles_m * tiles_n;
-    const int xcd = L & 7;
-    const int j = L >> 3;
-    const int per = T >> 3, extra = T & 7;
-    const int t = xcd * per + min(xcd, extra) + j;
-    constexpr int GM = 8;
-    const int group = t / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gm = min(GM, tiles_m - first_m);
-    const int in = t - group * GM * tiles_n;
-    tm = first_m + in % gm;
-    tn = in / gm;
 }
 
 // 32x32 tile family (large M), built on v_mfma_i32_32x32x32_i8 (the

@@ -138,6 +138,20 @@ struct LinearPlan {
 
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
 
+// Comparison GEMMs (W8A8 per-channel, W4A4 per-group with partial-sum
+// scaling) on the 32x32 tile skeleton.
+constexpr int kVariantW8A8 = 1;
+constexpr int kVariantW4A4 = 2;
+struct VariantPlan {
+    bool valid;         // false: QOQ_VARIANT_CONFIG names no compiled configuration
+    int fmt;
+    int mt, cb, pb, pa, nw;
+    int grid_x;
+};
+VariantPlan plan_variant(int fmt, int64_t M, int64_t N, int64_t K);
+int64_t w4a4_rows_padded(int64_t M);
+int64_t w4a4_act_bytes(int64_t M, int64_t K);
+
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed, uint16_t* s1,
                        uint8_t* cq4, int8_t* cs2, uint8_t* cz, bool from_canonical,
@@ -147,6 +161,17 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm(const GemmPlan& plan, const int8_t* x8, const float* s_x, int64_t M,
                        int64_t K, const uint8_t* packed, const uint16_t* s1, int64_t N,
                        uint16_t* y, int32_t* acc_debug, void* workspace, hipStream_t stream);
+hipError_t launch_w8a8_pack(const float* W, int64_t N, int64_t K, uint8_t* packed, uint16_t* s,
+                            hipStream_t stream);
+hipError_t launch_w4a4_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                            hipStream_t stream);
+hipError_t launch_w4a4_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* act,
+                                    hipStream_t stream);
+hipError_t launch_w8a8_gemm(const VariantPlan& p, const int8_t* x8, const float* s_x, int64_t M,
+                            int64_t K, const uint8_t* packed, const uint16_t* s, int64_t N,
+                            uint16_t* y, int32_t* acc_debug, hipStream_t stream);
+hipError_t launch_w4a4_gemm(const VariantPlan& p, const uint8_t* act, int64_t M, int64_t K,
+                            const uint8_t* packed, int64_t N, uint16_t* y, hipStream_t stream);
 hipError_t launch_linear_fused(const LinearPlan& plan, const uint16_t* x, int64_t M, int64_t K,
                                const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
                                int32_t* acc_debug, hipStream_t stream);

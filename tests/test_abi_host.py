@@ -18,7 +18,8 @@ P = 0x10000  # a 16-byte aligned address that is never dereferenced
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read()
+                   for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qoq_[a-z0-9_]+)\s*\(", text)))
 
@@ -33,6 +34,29 @@ def test_library_exports_every_declared_function():
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_variant_sizes_and_validation(monkeypatch):
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    L = qoq.lib()
+    assert L.qoq_w8a8_weight_bytes(4096, 4096) == 4096 * 4096
+    assert L.qoq_w8a8_weight_bytes(4008, 4096) == 0
+    assert L.qoq_w4a4_weight_bytes(4096, 4096) == qoq.qoq_packed_weight_bytes(4096, 4096)
+    # x4 codes (rows padded to 16, K/2 bytes each), then fp32 scales [K/128][M padded to 128]
+    assert L.qoq_w4a4_act_bytes(1, 4096) == 16 * 2048 + 32 * 128 * 4
+    assert L.qoq_w4a4_act_bytes(200, 256) == 208 * 128 + 2 * 256 * 4
+    assert L.qoq_w4a4_act_bytes(0, 4096) == 0 and L.qoq_w4a4_act_bytes(4, 100) == 0
+    assert L.qoq_w8a8_gemm(P, P, 4, 4000, P, P, 4096, P, None, None) == SHAPE
+    assert L.qoq_w8a8_gemm(None, P, 4, 4096, P, P, 4096, P, None, None) == NULL
+    assert L.qoq_w8a8_gemm(P + 1, P, 4, 4096, P, P, 4096, P, None, None) == ALIGN
+    assert L.qoq_w8a8_gemm(P, P, 0, 4096, P, P, 4096, P, None, None) == OK
+    assert L.qoq_w4a4_gemm(P, 4, 4096, P, 4008, P, None) == SHAPE
+    assert L.qoq_w4a4_gemm(P, 4, 4096, None, 4096, P, None) == NULL
+    assert L.qoq_w4a4_quantize_act(P, 4, 200, P, None) == SHAPE
+    assert L.qoq_w4a4_quantize_act(P + 2, 4, 256, P, None) == ALIGN
+    monkeypatch.setenv("QOQ_VARIANT_CONFIG", "9,9,9,9,9")
+    assert L.qoq_w8a8_gemm(P, P, 4, 4096, P, P, 4096, P, None, None) == 8
+    assert L.qoq_w4a4_gemm(P, 4, 4096, P, 4096, P, None) == 8
 
 
 def test_status_strings():

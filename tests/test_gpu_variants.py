@@ -1,0 +1,108 @@
+"""The comparison GEMMs (W8A8 per-channel; W4A4 per-group with partial-sum
+scaling) against their oracle: codes and scales bit-exact (read through the
+documented layouts), W8A8 INT32 accumulators bit-exact, W8A8 fp16 output
+within the QoQ tolerance, W4A4 fp16 output within the error bound of its fp32
+accumulation over groups."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from act_layout import act_rows
+from variant_layout import w4_codes_scales, w8_codes, x4_codes_scales
+
+qoq = pytest.importorskip("bit_integer_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SHAPES = [(1, 128, 16), (5, 640, 208), (37, 384, 48), (64, 2048, 528), (100, 640, 208),
+          (300, 1152, 528), (257, 256, 1040)]
+W8_CONFIGS = ["4,2,2,2,4", "4,2,2,1,8", "4,1,2,1,8", "2,2,2,2,4", "2,1,4,2,4", "1,1,4,3,4"]
+W4_CONFIGS = ["2,1,2,2,4", "2,1,2,1,8", "1,1,2,3,4", "2,2,2,2,4"]
+
+
+def _half(X):
+    return torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV)
+
+
+def _w8(M, K, N, monkeypatch, cfg=None):
+    W, X, _ = wl.make_inputs(M, K, N, seed=3 * M + K + N)
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    packed, s = qoq.w8a8_pack_weights(torch.from_numpy(W).to(DEV))
+    x8, s_x = qoq.quantize_act(_half(X))
+    if cfg:
+        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+    print(f"\n[gpu-case] w8a8 cfg={cfg} M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w8a8_gemm(x8, s_x, packed, s, N, acc_debug=True)
+    torch.cuda.synchronize()
+    ref = oracle.w8a8_linear(X, W)
+    assert np.array_equal(w8_codes(packed.cpu().numpy(), N, K), ref["q8"]), "codes"
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), ref["s"].view(np.uint16)), "scales"
+    assert np.array_equal(act_rows(x8, M), ref["x8"])
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"]), "acc"
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
+def _w4(M, K, N, monkeypatch, cfg=None):
+    W, X, _ = wl.make_inputs(M, K, N, seed=5 * M + K + N)
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    packed = qoq.w4a4_pack_weights(torch.from_numpy(W).to(DEV))
+    act = qoq.w4a4_quantize_act(_half(X))
+    if cfg:
+        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+    print(f"\n[gpu-case] w4a4 cfg={cfg} M={M} K={K} N={N}", flush=True)
+    y = qoq.w4a4_gemm(act, M, K, packed, N)
+    torch.cuda.synchronize()
+    ref = oracle.w4a4_linear(X, W)
+    codes, sc = w4_codes_scales(packed.cpu().numpy(), N, K)
+    assert np.array_equal(codes, ref["wq"]), "weight codes"
+    assert np.array_equal(sc.view(np.uint16), ref["s_w"].view(np.uint16)), "weight scales"
+    xq, s_a = x4_codes_scales(act.cpu().numpy(), M, K)
+    assert np.array_equal(xq, ref["xq"]), "activation codes"
+    assert np.array_equal(s_a.view(np.uint32), ref["s_a"].view(np.uint32)), "activation scales"
+    # fp32 accumulation of K/128 scaled partial sums, then one fp16 rounding
+    ng = K // 128
+    yy = y.cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -11 * np.abs(ref["y"]) + (ng + 2) * 2.0 ** -22 * ref["term_abs"] + 2.0 ** -24
+    bad = np.abs(yy - ref["y"]) > tol
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound, first at {np.argwhere(bad)[:3]}"
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w8a8_default(M, K, N, monkeypatch):
+    _w8(M, K, N, monkeypatch)
+
+
+@pytest.mark.parametrize("cfg", W8_CONFIGS)
+def test_w8a8_every_config(cfg, monkeypatch):
+    for (M, K, N) in [(37, 384, 48), (300, 1152, 528)]:
+        _w8(M, K, N, monkeypatch, cfg)
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w4a4_default(M, K, N, monkeypatch):
+    _w4(M, K, N, monkeypatch)
+
+
+@pytest.mark.parametrize("cfg", W4_CONFIGS)
+def test_w4a4_every_config(cfg, monkeypatch):
+    for (M, K, N) in [(37, 384, 48), (300, 1152, 528)]:
+        _w4(M, K, N, monkeypatch, cfg)
+
+
+def test_w4a4_zero_groups(monkeypatch):
+    W, X, _ = wl.make_inputs(20, 512, 64, seed=9)
+    W[3, 128:256] = 0
+    X[7, 256:384] = 0
+    X[11] = 0
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    packed = qoq.w4a4_pack_weights(torch.from_numpy(W).to(DEV))
+    act = qoq.w4a4_quantize_act(_half(X))
+    y = qoq.w4a4_gemm(act, 20, 512, packed, 64)
+    ref = oracle.w4a4_linear(X, W)
+    tol = 2.0 ** -11 * np.abs(ref["y"]) + 6 * 2.0 ** -22 * ref["term_abs"] + 2.0 ** -24
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref["y"]) <= tol)
+    assert torch.all(y[11] == 0)

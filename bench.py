@@ -61,6 +61,8 @@ def parse():
                    help="comma list; the decode step is always the headline")
     p.add_argument("--shape-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the W8A8 / W4A4 comparison GEMMs")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
 
@@ -393,6 +395,8 @@ def main():
             del ck, pwk
             torch.cuda.empty_cache()
 
+    variants = None if args.no_variants else variant_comparison(torch, qoq, blocker, dev, ws,
+                                                                args.shape_iters)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dw, shape, args.cpu_seconds)
     traffic = traffic_record()
 
@@ -434,10 +438,91 @@ def main():
                  "fp32_read_gbs": round(N * K * 4 / pack_t / 1e9, 1)},
         "copy_reference": copy_ref,
         "shapes": shapes_out,
+        "variants": variants,
         "host_cores": len(os.sched_getaffinity(0)),
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
+
+
+VARIANT_SHAPES = [("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),
+                  ("qwen15_72b", "gate_up", 1024), ("qwen15_72b", "down", 1024)]
+
+
+def variant_comparison(torch, qoq, blocker, dev, ws, iters):
+    """The dequantization-overhead comparison: the W4A8 QoQ GEMM against the
+    W8A8 per-channel GEMM (no dequantization, twice the weight bytes) and the
+    per-group W4A4 GEMM (INT4 weights and activations, every group's INT32
+    partial sums converted and scaled in the main loop), GEMM kernels alone on
+    pre-quantized inputs, each at its default launch plan and all three at
+    one common 64 x 128 tile (4 waves, 2 workgroups per CU) so that only the
+    format differs."""
+    import os as _os
+    out = []
+    common = "2,1,2,2,4"
+    for key, sname, M in VARIANT_SHAPES:
+        w = wl.WORKLOADS[key]
+        shp = next(x for x in w.shapes if x.name == sname)
+        K, N = shp.K, shp.N
+        W, X, _ = wl.make_case(w, shp, M)
+        Wd = torch.from_numpy(W).to(dev)
+        del W
+        xd = to_half_device(torch, X, dev)
+        pw = qoq.pack_weights(Wd)
+        p8, s8 = qoq.w8a8_pack_weights(Wd)
+        p4 = qoq.w4a4_pack_weights(Wd)
+        del Wd
+        x8, s_x = qoq.quantize_act(xd)
+        a4 = qoq.w4a4_quantize_act(xd)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        L = qoq.lib()
+        cq = rotated_copies(pw)
+        n8 = int(min(512, max(2, -(-ROTATE_BYTES // p8.numel()))))
+        c8 = [p8] + [p8.clone() for _ in range(n8 - 1)]
+        c4 = rotated_copies(qoq.PackedWeight(p4, pw.s1, N, K))
+        st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+        def q_calls(cfg):
+            calls = [GemmCall(qoq, torch, x8, s_x, cp, pw.s1, N, y, ws) for cp in cq]
+            return calls
+
+        def w8_calls():
+            return [lambda cp=cp: L.qoq_w8a8_gemm(x8.data_ptr(), s_x.data_ptr(), M, K, cp.data_ptr(),
+                                                  s8.data_ptr(), N, y.data_ptr(), None, st())
+                    for cp in c8]
+
+        def w4_calls():
+            return [lambda cp=cp: L.qoq_w4a4_gemm(a4.data_ptr(), M, K, cp.data_ptr(), N, y.data_ptr(),
+                                                  st()) for cp in c4]
+
+        rec = dict(workload=key, shape=sname, M=M, K=K, N=N)
+        ops = wl.algorithmic_ops(M, K, N)
+        for label, env_key, env_val, make in (
+                ("w4a8_qoq", None, None, lambda: q_calls(None)),
+                ("w8a8", None, None, w8_calls),
+                ("w4a4", None, None, w4_calls),
+                ("w4a8_qoq_common_tile", "QOQ_GEMM_CONFIG", "tile32," + common, lambda: q_calls(None)),
+                ("w8a8_common_tile", "QOQ_VARIANT_CONFIG", common, w8_calls),
+                ("w4a4_common_tile", "QOQ_VARIANT_CONFIG", common, w4_calls)):
+            saved = {k: _os.environ.pop(k, None) for k in ("QOQ_GEMM_CONFIG", "QOQ_VARIANT_CONFIG")}
+            if env_key:
+                _os.environ[env_key] = env_val
+            try:
+                calls = make()
+                for cl in calls[:2]:
+                    cl()
+                t = per_launch_times(torch, blocker, [calls], max(iters, len(calls)))[0]
+                rec[label + "_us"] = round(t * 1e6, 2)
+                rec[label + "_tops"] = round(ops / t / 1e12, 1)
+            finally:
+                for k, v in saved.items():
+                    _os.environ.pop(k, None)
+                    if v is not None:
+                        _os.environ[k] = v
+        out.append(rec)
+        del cq, c8, c4, pw, p8, p4
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(dw, shape, budget_s):

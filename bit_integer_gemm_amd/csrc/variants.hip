@@ -486,7 +486,7 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_variant_kernel(
 // Compiled configurations: (MT, CB, PB, workgroups per CU, waves).
 #define QOQ_W8_CONFIGS(X)                                                                 \
     X(4, 2, 2, 2, 4) X(4, 2, 2, 1, 8) X(4, 1, 2, 1, 8) X(2, 2, 2, 2, 4) X(2, 1, 4, 2, 4)    \
-    X(1, 1, 4, 3, 4)
+    X(1, 1, 4, 3, 4) X(2, 1, 2, 2, 4)
 #define QOQ_W4A4_CONFIGS(X)                                                               \
     X(2, 1, 2, 2, 4) X(2, 1, 2, 1, 8) X(1, 1, 2, 3, 4) X(2, 2, 2, 2, 4)
 

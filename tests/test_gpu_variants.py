@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SHAPES = [(1, 128, 16), (5, 640, 208), (37, 384, 48), (64, 2048, 528), (100, 640, 208),
           (300, 1152, 528), (257, 256, 1040)]
-W8_CONFIGS = ["4,2,2,2,4", "4,2,2,1,8", "4,1,2,1,8", "2,2,2,2,4", "2,1,4,2,4", "1,1,4,3,4"]
+W8_CONFIGS = ["4,2,2,2,4", "4,2,2,1,8", "4,1,2,1,8", "2,2,2,2,4", "2,1,4,2,4", "1,1,4,3,4",
+              "2,1,2,2,4"]
 W4_CONFIGS = ["2,1,2,2,4", "2,1,2,1,8", "1,1,2,3,4", "2,2,2,2,4"]
 
 

@@ -6,4 +6,5 @@ from .qoq_oracle import (PROTECT, ACT_MAX, Q4_MAX, rne_div, ceil_div,  # noqa: F
                          epilogue, w4a8_linear)
 from .variants import (W8_MAX, INT4_MAX, w8a8_quantize_weights, w8a8_linear,  # noqa: F401
                        w4a4_quantize_weights, w4a4_quantize_act, w4a4_partial_sums,
-                       w4a4_linear)
+                       w4a4_linear, w4a16_quantize_weights, w4a16_dequantize,
+                       w4a16_linear)

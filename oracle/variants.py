@@ -4,12 +4,14 @@ TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
 executes this module: only the tests and the benchmark's CPU-baseline leg
 do. It shares no code with the HIP library.
 
-The pages measure QoQ's W4A8 GEMM against two other low-bit GEMM families
+The pages measure QoQ's W4A8 GEMM against other low-bit GEMM families
 ("QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
 Serving", velog study notes, sections "문제 정의" and "Background"; the QServe
 abstract): W8A8 with per-channel weights and per-token activations, whose
-GEMM needs no dequantization at all, and per-group W4A4, whose INT32 partial
-sums must be converted and scaled inside the main loop for every group. The
+GEMM needs no dequantization at all; weight-only W4A16, whose 4-bit weights
+are dequantized to fp16 for fp16 matrix units; and per-group W4A4, whose
+INT32 partial sums must be converted and scaled inside the main loop for
+every group. The
 pages give no arithmetic for either; the readings below are the plainest
 ones the rest supports (listed again in the design notes):
 
@@ -18,6 +20,12 @@ ones the rest supports (listed again in the design notes):
   clamp(rne(fp32(w / fp32(s))), -127, 127) -- the QoQ level-1 step with the
   whole INT8 range instead of the protective range; activations as QoQ's
   (per-token symmetric INT8); y = acc * s_x[m] * s[n].
+* W4A16: per-group (128 inputs) asymmetric UINT4 weights with an fp16 scale
+  and a UINT4 zero (the weight-only format the pages' W4A16 baselines serve):
+  lo = min(0, min w), hi = max(0, max w), s = fp16(fp32(fp32(hi - lo) / 15)),
+  z = clamp(rne(fp32(-lo / fp32(s))), 0, 15), q = clamp(rne(fp32(w /
+  fp32(s))) + z, 0, 15) (all-zero group: s = 0, q = z = 0); dequantized to
+  fp16 as w16 = fp16((q - z) * s); activations stay fp16; y = x @ w16^T.
 * W4A4: per-group (128 inputs) symmetric INT4 in [-7, 7] for both operands:
   weights with an fp16 scale per (channel, group), s_w = fp16(fp32(a / 7)),
   codes clamp(rne(fp32(w / fp32(s_w))), -7, 7); activations with an fp32
@@ -130,3 +138,48 @@ def w4a4_linear(x, W, group=128):
     terms = P * scale
     return {"y": terms.sum(axis=2), "term_abs": np.abs(terms).sum(axis=2), "P": P,
             "xq": xq, "s_a": s_a, "wq": wq, "s_w": s_w}
+
+
+# --------------------------------------------------------------------------
+# W4A16: per-group UINT4 weights dequantized to fp16, fp16 activations
+# --------------------------------------------------------------------------
+def w4a16_quantize_weights(W, group=128):
+    """Per-(channel, group) asymmetric UINT4 with fp16 scale and UINT4 zero.
+
+    Returns q uint8 [N, K] (0..15), s float16 [N, K/group], z uint8 [N, K/group].
+    """
+    W = np.asarray(W, dtype=np.float32)
+    g = _grouped(W, group)
+    lo = np.minimum(np.float32(0), g.min(axis=2))
+    hi = np.maximum(np.float32(0), g.max(axis=2))
+    s = ((hi - lo) / np.float32(15)).astype(np.float16)        # fp32 ops, RNE to fp16
+    s_back = s.astype(np.float32)
+    z = np.zeros(s.shape, dtype=np.int64)
+    q = np.zeros(g.shape, dtype=np.int64)
+    live = s_back != 0
+    if np.any(live):
+        z[live] = np.clip(np.rint(-lo[live] / s_back[live]), 0, 15).astype(np.int64)
+        codes = np.rint(g[live] / s_back[live][:, None]).astype(np.int64)
+        q[live] = np.clip(codes + z[live][:, None], 0, 15)
+    return q.reshape(W.shape).astype(np.uint8), s, z.astype(np.uint8)
+
+
+def w4a16_dequantize(q, s, z, group=128):
+    """w16 = fp16((q - z) * s): the product of a small integer and an fp16
+    value is exact in fp64, then rounded once to fp16."""
+    q = _grouped(np.asarray(q, dtype=np.int64), group)
+    prod = (q - np.asarray(z, dtype=np.int64)[:, :, None]) * \
+        np.asarray(s, dtype=np.float16).astype(np.float64)[:, :, None]
+    n_rows = q.shape[0]
+    return prod.reshape(n_rows, -1).astype(np.float16)
+
+
+def w4a16_linear(x, W, group=128):
+    """Whole W4A16 path: y = x16 @ w16^T in fp64, with term_abs =
+    |x16| @ |w16|^T (the scale of any accumulation order's rounding)."""
+    q, s, z = w4a16_quantize_weights(W, group)
+    w16 = w4a16_dequantize(q, s, z, group)
+    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    wf = w16.astype(np.float64)
+    return {"y": xf @ wf.T, "term_abs": np.abs(xf) @ np.abs(wf).T, "q": q, "s": s, "z": z,
+            "w16": w16}

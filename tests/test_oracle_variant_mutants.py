@@ -31,6 +31,18 @@ MUTANTS = [
     ("partial sums drop last input", 'return np.einsum("mgk,ngk->mng", a, b)',
      'return np.einsum("mgk,ngk->mng", a[:, :, :-1], b[:, :, :-1])'),
     ("y drops weight scale", "* s_w.astype(np.float64)[None, :, :]", "* 1.0"),
+    ("w4a16 range without zero", "lo = np.minimum(np.float32(0), g.min(axis=2))", "lo = g.min(axis=2)"),
+    ("w4a16 scale over 16 levels", "s = ((hi - lo) / np.float32(15)).astype(np.float16)",
+     "s = ((hi - lo) / np.float32(16)).astype(np.float16)"),
+    ("w4a16 scale kept fp32", "s = ((hi - lo) / np.float32(15)).astype(np.float16)",
+     "s = ((hi - lo) / np.float32(15))"),
+    ("w4a16 zero sign", "np.rint(-lo[live] / s_back[live])", "np.rint(lo[live] / s_back[live])"),
+    ("w4a16 codes without zero", "q[live] = np.clip(codes + z[live][:, None], 0, 15)",
+     "q[live] = np.clip(codes, 0, 15)"),
+    ("w4a16 dequant adds zero", "prod = (q - np.asarray(z, dtype=np.int64)[:, :, None])",
+     "prod = (q + np.asarray(z, dtype=np.int64)[:, :, None])"),
+    ("w4a16 dequant kept exact", "return prod.reshape(n_rows, -1).astype(np.float16)",
+     "return prod.reshape(n_rows, -1)"),
     ("y drops token scale", "scale = s_a.astype(np.float64)[:, None, :]",
      "scale = np.ones_like(s_a, dtype=np.float64)[:, None, :]"),
 ]

@@ -168,6 +168,56 @@ def pin_w4a4_bounds(O):
     assert np.all(np.abs(W - wq * sw) <= sw * (0.5 + 7 * 2.0 ** -11) + 1e-12)
 
 
+def pin_w4a16_exact(O):
+    """Scales, zeros, codes and fp16 dequantized weights equal the exact
+    derivation, including a one-signed group and an all-zero group."""
+    G = 8
+    W = _rng_case(18, 3, 32, zero_group=(1, 2), group=G)
+    W[2, 0:8] = np.abs(W[2, 0:8]) + np.float32(0.01)       # all positive: lo = 0
+    q, s, z = O.w4a16_quantize_weights(W, G)
+    w16 = O.w4a16_dequantize(q, s, z, G)
+    for n in range(3):
+        for g in range(4):
+            grp = [F(float(v)) for v in W[n, g * G:(g + 1) * G]]
+            lo, hi = min(F(0), min(grp)), max(F(0), max(grp))
+            s_ref = fp16(fp32(fp32(hi - lo) / 15))
+            assert F(float(s[n, g])) == s_ref, (n, g)
+            if s_ref == 0:
+                assert z[n, g] == 0 and not np.any(q[n, g * G:(g + 1) * G])
+                continue
+            z_ref = _clamp(round_half_even(fp32(-lo / s_ref)), 0, 15)
+            assert int(z[n, g]) == z_ref, (n, g)
+            for i, v in enumerate(grp):
+                q_ref = _clamp(round_half_even(fp32(v / s_ref)) + z_ref, 0, 15)
+                assert int(q[n, g * G + i]) == q_ref, (n, g, i)
+                assert F(float(w16[n, g * G + i])) == fp16((q_ref - z_ref) * s_ref)
+
+
+def pin_w4a16_linear_brute(O):
+    """y and term_abs by pure-Python loops over the fp16 values."""
+    rng = np.random.default_rng(19)
+    W = (0.05 * rng.standard_normal((3, 16))).astype(np.float32)
+    X = rng.standard_normal((2, 16)).astype(np.float16)
+    r = O.w4a16_linear(X, W, 8)
+    for m in range(2):
+        for n in range(3):
+            terms = [F(float(X[m, k])) * F(float(r["w16"][n, k])) for k in range(16)]
+            assert abs(F(float(r["y"][m, n])) - sum(terms)) <= F(1, 2 ** 40)
+            assert abs(F(float(r["term_abs"][m, n])) - sum(abs(t) for t in terms)) <= F(1, 2 ** 40)
+
+
+def pin_w4a16_bounds(O):
+    """|w - w16| <= s/2 plus fp16 rounding for weights inside [lo, hi];
+    codes in [0, 15]; the zero code reproduces 0 up to rounding."""
+    rng = np.random.default_rng(20)
+    W = (0.02 * rng.standard_normal((4, 256))).astype(np.float32)
+    q, s, z = O.w4a16_quantize_weights(W, 128)
+    w16 = O.w4a16_dequantize(q, s, z, 128).astype(np.float64)
+    sf = np.repeat(s.astype(np.float64), 128, axis=1)
+    assert q.max() <= 15
+    assert np.all(np.abs(W - w16) <= sf * 0.5 * (1 + 2.0 ** -8) + np.abs(W) * 2.0 ** -10)
+
+
 VARIANT_PINS = [pin_w8a8_exact, pin_w8a8_linear_brute, pin_w4a4_exact,
                 pin_w4a4_partial_sums_brute, pin_w4a4_dequant_matmul, pin_w4a4_whole_row_group,
-                pin_w4a4_bounds]
+                pin_w4a4_bounds, pin_w4a16_exact, pin_w4a16_linear_brute, pin_w4a16_bounds]

@@ -451,12 +451,13 @@ VARIANT_SHAPES = [("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("pr
 
 def variant_comparison(torch, qoq, blocker, dev, ws, iters):
     """The dequantization-overhead comparison: the W4A8 QoQ GEMM against the
-    W8A8 per-channel GEMM (no dequantization, twice the weight bytes) and the
+    W8A8 per-channel GEMM (no dequantization, twice the weight bytes), the
     per-group W4A4 GEMM (INT4 weights and activations, every group's INT32
-    partial sums converted and scaled in the main loop), GEMM kernels alone on
-    pre-quantized inputs, each at its default launch plan and all three at
-    one common 64 x 128 tile (4 waves, 2 workgroups per CU) so that only the
-    format differs."""
+    partial sums converted and scaled in the main loop) and the weight-only
+    W4A16 GEMM (UINT4 weights dequantized to fp16 for fp16 MFMA, fp16
+    activations), GEMM kernels alone on pre-quantized inputs, each at its
+    default launch plan and all four at one common 64 x 128 tile (4 waves, 2
+    workgroups per CU) so that only the format differs."""
     import os as _os
     out = []
     common = "2,1,2,2,4"
@@ -471,6 +472,7 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
         pw = qoq.pack_weights(Wd)
         p8, s8 = qoq.w8a8_pack_weights(Wd)
         p4 = qoq.w4a4_pack_weights(Wd)
+        p16 = qoq.w4a16_pack_weights(Wd)
         del Wd
         x8, s_x = qoq.quantize_act(xd)
         a4 = qoq.w4a4_quantize_act(xd)
@@ -480,6 +482,8 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
         n8 = int(min(512, max(2, -(-ROTATE_BYTES // p8.numel()))))
         c8 = [p8] + [p8.clone() for _ in range(n8 - 1)]
         c4 = rotated_copies(qoq.PackedWeight(p4, pw.s1, N, K))
+        n16 = int(min(512, max(2, -(-ROTATE_BYTES // p16.numel()))))
+        c16 = [p16] + [p16.clone() for _ in range(n16 - 1)]
         st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
 
         def q_calls(cfg):
@@ -495,22 +499,30 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
             return [lambda cp=cp: L.qoq_w4a4_gemm(a4.data_ptr(), M, K, cp.data_ptr(), N, y.data_ptr(),
                                                   st()) for cp in c4]
 
+        def w16_calls():
+            return [lambda cp=cp: L.qoq_w4a16_gemm(xd.data_ptr(), M, K, cp.data_ptr(), N,
+                                                   y.data_ptr(), st()) for cp in c16]
+
         rec = dict(workload=key, shape=sname, M=M, K=K, N=N)
         ops = wl.algorithmic_ops(M, K, N)
         for label, env_key, env_val, make in (
                 ("w4a8_qoq", None, None, lambda: q_calls(None)),
                 ("w8a8", None, None, w8_calls),
                 ("w4a4", None, None, w4_calls),
+                ("w4a16", None, None, w16_calls),
                 ("w4a8_qoq_common_tile", "QOQ_GEMM_CONFIG", "tile32," + common, lambda: q_calls(None)),
                 ("w8a8_common_tile", "QOQ_VARIANT_CONFIG", common, w8_calls),
-                ("w4a4_common_tile", "QOQ_VARIANT_CONFIG", common, w4_calls)):
+                ("w4a4_common_tile", "QOQ_VARIANT_CONFIG", common, w4_calls),
+                ("w4a16_common_tile", "QOQ_VARIANT_CONFIG", common, w16_calls)):
             saved = {k: _os.environ.pop(k, None) for k in ("QOQ_GEMM_CONFIG", "QOQ_VARIANT_CONFIG")}
             if env_key:
                 _os.environ[env_key] = env_val
             try:
                 calls = make()
                 for cl in calls[:2]:
-                    cl()
+                    rc = cl()
+                    if rc:
+                        raise RuntimeError(f"{label}: {qoq.qoq_status_string(rc)}")
                 t = per_launch_times(torch, blocker, [calls], max(iters, len(calls)))[0]
                 rec[label + "_us"] = round(t * 1e6, 2)
                 rec[label + "_tops"] = round(ops / t / 1e12, 1)
@@ -520,7 +532,7 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
                     if v is not None:
                         _os.environ[k] = v
         out.append(rec)
-        del cq, c8, c4, pw, p8, p4
+        del cq, c8, c4, c16, pw, p8, p4, p16
         torch.cuda.empty_cache()
     return out
 

@@ -33,6 +33,7 @@ __all__ = [
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
     "Workspace", "empty_act", "w4a8_linear",
     "w8a8_pack_weights", "w8a8_gemm", "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_gemm",
+    "w4a16_pack_weights", "w4a16_gemm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -104,6 +105,12 @@ def lib() -> ctypes.CDLL:
         L.qoq_w4a4_quantize_act.restype = ctypes.c_int
         L.qoq_w4a4_gemm.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         L.qoq_w4a4_gemm.restype = ctypes.c_int
+        L.qoq_w4a16_weight_bytes.argtypes = [i64, i64]
+        L.qoq_w4a16_weight_bytes.restype = sz
+        L.qoq_w4a16_pack_weights.argtypes = [vp, i64, i64, vp, vp]
+        L.qoq_w4a16_pack_weights.restype = ctypes.c_int
+        L.qoq_w4a16_gemm.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        L.qoq_w4a16_gemm.restype = ctypes.c_int
         L.qoq_status_string.argtypes = [ctypes.c_int]
         L.qoq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -343,7 +350,8 @@ def w4a8_linear(x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
 
 
 # ---------------------------------------------------------------------------
-# comparison GEMMs (W8A8 per-channel; W4A4 per-group with partial-sum scaling)
+# comparison GEMMs (W8A8 per-channel; W4A4 per-group with partial-sum
+# scaling; W4A16 weight-only with fp16 dequantization)
 # ---------------------------------------------------------------------------
 def w8a8_pack_weights(W: torch.Tensor):
     """Per-channel INT8 weights of W fp32 [N, K] -> (packed uint8, s fp16 [N])."""
@@ -405,4 +413,30 @@ def w4a4_gemm(act: torch.Tensor, M: int, K: int, packed: torch.Tensor, N: int) -
     y = torch.empty((M, N), dtype=torch.float16, device=act.device)
     _check(lib().qoq_w4a4_gemm(act.data_ptr(), M, K, packed.data_ptr(), N, y.data_ptr(),
                                _stream(act.device)), "qoq_w4a4_gemm")
+    return y
+
+
+def w4a16_pack_weights(W: torch.Tensor) -> torch.Tensor:
+    """Per-(channel, group) UINT4 weights with fp16 scale and zero of W fp32
+    [N, K] -> packed uint8."""
+    _need_gpu(W, "W", torch.float32)
+    N, K = W.shape
+    nbytes = int(lib().qoq_w4a16_weight_bytes(N, K))
+    if nbytes == 0:
+        raise QoQError(2, "qoq_w4a16_pack_weights")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    _check(lib().qoq_w4a16_pack_weights(W.data_ptr(), N, K, packed.data_ptr(), _stream(W.device)),
+           "qoq_w4a16_pack_weights")
+    return packed
+
+
+def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, N: int) -> torch.Tensor:
+    """W4A16 GEMM on fp16 x [M, K]: weights dequantized to fp16 in the main
+    loop, fp32 accumulation, y fp16 [M, N]."""
+    _need_gpu(x, "x", torch.float16)
+    _need_gpu(packed, "packed", torch.uint8)
+    M, K = x.shape
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check(lib().qoq_w4a16_gemm(x.data_ptr(), M, K, packed.data_ptr(), N, y.data_ptr(),
+                                _stream(x.device)), "qoq_w4a16_gemm")
     return y

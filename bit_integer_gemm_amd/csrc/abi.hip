@@ -226,6 +226,39 @@ qoq_status qoq_w4a4_gemm(const void* act, int64_t M, int64_t K, const void* pack
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
+size_t qoq_w4a16_weight_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K, qoq::kGroup) != QOQ_OK) return 0;
+    const qoq::PackedLayout L = qoq::packed_layout(N, K);
+    return size_t(L.total + L.rec_bytes);
+}
+
+qoq_status qoq_w4a16_pack_weights(const float* W, int64_t N, int64_t K, void* packed,
+                                  void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (W == nullptr || packed == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(W) || misaligned(packed)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_w4a16_pack(W, N, K, static_cast<uint8_t*>(packed),
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const void* packed, int64_t N,
+                          uint16_t* y, void* stream) {
+    const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x == nullptr || packed == nullptr || y == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(x) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
+    if (N * K / 2 >= (int64_t(1) << 31) || M * K * 2 >= (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    const qoq::VariantPlan plan = qoq::plan_variant(qoq::kVariantW4A16, M, N, K);
+    if (!plan.valid) return QOQ_ERR_CONFIG;
+    const hipError_t e = qoq::launch_w4a16_gemm(plan, x, M, K, static_cast<const uint8_t*>(packed),
+                                                N, y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
 const char* qoq_status_string(int status) {
     switch (status) {
         case QOQ_OK: return "ok";

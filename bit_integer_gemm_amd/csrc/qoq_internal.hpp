@@ -142,6 +142,7 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
 // scaling) on the 32x32 tile skeleton.
 constexpr int kVariantW8A8 = 1;
 constexpr int kVariantW4A4 = 2;
+constexpr int kVariantW4A16 = 3;
 struct VariantPlan {
     bool valid;         // false: QOQ_VARIANT_CONFIG names no compiled configuration
     int fmt;
@@ -165,6 +166,10 @@ hipError_t launch_w8a8_pack(const float* W, int64_t N, int64_t K, uint8_t* packe
                             hipStream_t stream);
 hipError_t launch_w4a4_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
                             hipStream_t stream);
+hipError_t launch_w4a16_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                             hipStream_t stream);
+hipError_t launch_w4a16_gemm(const VariantPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                             const uint8_t* packed, int64_t N, uint16_t* y, hipStream_t stream);
 hipError_t launch_w4a4_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* act,
                                     hipStream_t stream);
 hipError_t launch_w8a8_gemm(const VariantPlan& p, const int8_t* x8, const float* s_x, int64_t M,

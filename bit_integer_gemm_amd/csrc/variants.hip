@@ -19,6 +19,10 @@
 //   W8A8 act       QoQ's x8 tile layout and s_x (qoq_quantize_act).
 //   W4A4 weights   QoQ's nibble layout with u = code + 8 in each nibble and
 //                  the fp16 group scale in each group's 2-byte record slot.
+//   W4A16 weights  QoQ's nibble layout with u = q (UINT4 code), then two
+//                  record regions of QoQ's record shape: the fp16 group
+//                  scales, then the group zeros (uint16).
+//   W4A16 act      fp16 x, row-major [M, K] (no quantization).
 //   W4A4 act       x4 tile layout: row m, inputs 16j .. 16j + 15 are 8 bytes
 //                  at ((m / 16) * (K / 16) + j) * 128 + (m % 16) * 8, byte b
 //                  holding u(16j + b) | u(16j + 8 + b) << 4 with u = code + 8;
@@ -40,6 +44,7 @@ constexpr int kInt4Max = 7;
 constexpr int kW8BlockBytes = 2048;
 constexpr int kFmtW8 = 1;
 constexpr int kFmtW4A4 = 2;
+constexpr int kFmtW4A16 = 3;
 
 // ---------------------------------------------------------------------------
 // weight and activation quantizers
@@ -183,6 +188,51 @@ __global__ void __launch_bounds__(256) a4_quant_kernel(const uint16_t* __restric
         }
         *reinterpret_cast<uint2*>(out + (k0 >> 4) * 128) = uint2{lo, hi};
         if ((threadIdx.x & 7) == 0) s_a[(k0 >> 7) * Mp + m] = a > 0.0f ? a / float(kInt4Max) : 0.0f;
+    }
+}
+
+// W4A16 weights: one wave per (channel, group); lane i handles inputs
+// 128g + i and 128g + 64 + i. Range including 0, fp16 scale, UINT4 zero.
+__global__ void __launch_bounds__(256) w4a16_pack_kernel(const float* __restrict__ W, int64_t N,
+                                                         int64_t K, uint8_t* __restrict__ nib,
+                                                         uint8_t* __restrict__ srec,
+                                                         uint8_t* __restrict__ zrec, int64_t ng8) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t ng = K / kGroup;
+    if (wave >= N * ng) return;
+    const int c = int(wave & 15);
+    const int64_t rest = wave >> 4;
+    const int64_t g = rest % ng;
+    const int64_t nb = rest / ng;
+    const int64_t n = nb * kBlockCols + c;
+    const int64_t k0 = n * K + g * kGroup + lane;
+    const float w0 = W[k0], w1 = W[k0 + 64];
+    float lo = fminf(0.0f, fminf(w0, w1)), hi = fmaxf(0.0f, fmaxf(w0, w1));
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    }
+    const uint16_t sbits = __half_as_ushort(__float2half_rn((hi - lo) / 15.0f));
+    const float sc = h2f(sbits);
+    int q0 = 0, q1 = 0, z = 0;
+    if (sc != 0.0f) {
+        z = int(fminf(fmaxf(rintf(-lo / sc), 0.0f), 15.0f));
+        q0 = min(15, max(0, int(rintf(w0 / sc)) + z));
+        q1 = min(15, max(0, int(rintf(w1 / sc)) + z));
+    }
+    const int64_t block = nb * ng + g;
+    nib[block * kBlockBytes + 16 * (c + 16 * (lane >> 4)) + (lane & 15)] = uint8_t(q0 | (q1 << 4));
+    if (lane < kRecChunk) {
+        const int64_t gi = g + lane;
+        const bool mine = lane == 0;
+        const bool pad = (g == ng - 1) && lane > 0 && gi < ng8 * kRecChunk;
+        if (mine || pad) {
+            const int64_t off = ((nb * ng8 + gi / kRecChunk) * kBlockCols + c) * (kRecChunk * 2) +
+                                (gi % kRecChunk) * 2;
+            *reinterpret_cast<uint16_t*>(srec + off) = mine ? sbits : uint16_t(0);
+            *reinterpret_cast<uint16_t*>(zrec + off) = mine ? uint16_t(z) : uint16_t(0);
+        }
     }
 }
 
@@ -483,16 +533,224 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_variant_kernel(
     }
 }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Eight UINT4 codes, one per byte of the pair (w0, w1), low or high nibble ->
+// the eight fp16 weights fp16((q - z) * s) in byte order. 0x6400 | q is the
+// fp16 value 1024 + q, so (1024 + q) - (1024 + z) = q - z exactly, and one
+// fp16 multiply rounds the product once.
+template <bool kHigh>
+__device__ __forceinline__ v8h dequant_f16x8(uint32_t w0, uint32_t w1, h2 zz, h2 ss) {
+    const uint32_t w[2] = {w0, w1};
+    v8h r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            // bytes 2p, 2p + 1 of w[i] into the two 16-bit halves
+            const uint32_t t = __builtin_amdgcn_perm(0u, w[i], p ? 0x0c030c02u : 0x0c010c00u);
+            const uint32_t bits = ((kHigh ? t >> 4 : t) & 0x000F000Fu) | 0x64006400u;
+            const h2 v = (__builtin_bit_cast(h2, bits) - zz) * ss;
+            r[4 * i + 2 * p] = v[0];
+            r[4 * i + 2 * p + 1] = v[1];
+        }
+    }
+    return r;
+}
+
+// W4A16 GEMM: fp16 activations staged in LDS in v_mfma_f32_32x32x16_f16
+// fragment order (lane l: row l % 32, inputs 8 (l / 32) .. +7 of a 16-input
+// step), UINT4 weights dequantized to fp16 per step, fp32 accumulation, fp16
+// output. Same tile order, rings and epilogue as the integer kernels.
+template <int MT, int CB, int PB, int MINB, int NW>
+__global__ void __launch_bounds__(64 * NW, MINB) gemm_w4a16_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ srec, const uint8_t* __restrict__ zrec, int ng8, int N,
+    uint16_t* __restrict__ y) {
+    constexpr int AF = 8 * MT;                    // fragments per group (8 steps of 16)
+    constexpr int BM = 32 * MT, BNB = 2 * CB * NW;
+    constexpr int AL = BM / (4 * NW);             // 1 KiB row loads per wave per group
+    static_assert(AL >= 1 && BM % (4 * NW) == 0, "rows per wave");
+    static_assert(PB == 1 || PB == 2, "ring depth divides the unroll");
+    constexpr int kSlotsBytes = 2 * AF * 64 * 16;
+    constexpr int kStageBytes = NW * 32 * 32 * CB * 2;
+    __shared__ v4i lds_raw[(kSlotsBytes > kStageBytes ? kSlotsBytes : kStageBytes) / 16];
+    v4i (*As)[AF][64] = reinterpret_cast<v4i (*)[AF][64]>(lds_raw);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31;
+    const int q = lane >> 5;
+    const int c = lane & 15;
+    const int ng = K >> 7;
+    const int nbt = N >> 4;
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (nbt + BNB - 1) / BNB;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int nbw = tn * BNB + wave * 2 * CB;
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)x, (short)0, M * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)nib, (short)0, nbt * ng * kBlockBytes, 0x00020000);
+    const int rec_bytes = nbt * ng8 * (kBlockCols * kRecChunk * 2);
+    const __amdgpu_buffer_rsrc_t rsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)srec, (short)0, rec_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rzr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)zrec, (short)0, rec_bytes, 0x00020000);
+
+    // A staging: load u of this wave covers tile rows 4 (wave + NW u) + l / 16,
+    // bytes 16 (l % 16) of the row's 256-byte group chunk (inputs 8 (l % 16)
+    // ..), which is lane (row % 32) + 32 (l % 2) of fragment
+    // (row / 32, (l % 16) / 2). Rows past M read the last row.
+    int a_lane[AL], a_dst[AL];
+#pragma unroll
+    for (int u = 0; u < AL; ++u) {
+        const int row = 4 * (wave + NW * u) + (lane >> 4);
+        a_lane[u] = min(m0 + row, M - 1) * K * 2 + 16 * (lane & 15);
+        a_dst[u] = ((row >> 5) * 8 + ((lane & 15) >> 1)) * 64 + (row & 31) + 32 * (lane & 1);
+    }
+    int b_lane[CB], r_lane[CB];
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+        const int blk = min(nbw + 2 * t + (j >> 4), nbt - 1);
+        b_lane[t] = blk * ng * kBlockBytes + c * 16 + 8 * q;
+        r_lane[t] = (blk * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    }
+
+    v16f acc[MT][CB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][t][r] = 0.0f;
+
+    v4i ar[AL];
+    uint2 qn[PB][CB][4];        // per 32-column tile: block lanes c + 16h, 8 bytes each
+    uint32_t sz[PB][CB][2];     // fp16 scale bits, zero
+    auto load_a = [&](int g) {
+        g = min(g, ng - 1);
+#pragma unroll
+        for (int u = 0; u < AL; ++u)
+            ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane[u], g * 256, 0));
+    };
+    auto stage_a = [&](int slot) {
+        v4i* base = &As[slot][0][0];
+#pragma unroll
+        for (int u = 0; u < AL; ++u) base[a_dst[u]] = ar[u];
+    };
+    auto load_b = [&](int p, int g) {
+        g = min(g, ng - 1);
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                qn[p][t][h] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                    rb, b_lane[t], g * kBlockBytes + 256 * h, 0));
+            const int roff = (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2;
+            sz[p][t][0] = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rsr, r_lane[t], roff, 0));
+            sz[p][t][1] = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rzr, r_lane[t], roff, 0));
+        }
+    };
+    auto step = [&](int i, int u, bool full) {
+        if (i + 1 < ng) stage_a((u + 1) & 1);
+        load_a(i + 2);
+        uint2 bw[CB][4];
+        h2 zz[CB], ss[CB];
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) bw[t][h] = qn[u % PB][t][h];
+            const _Float16 s16 = __builtin_bit_cast(_Float16, uint16_t(sz[u % PB][t][0]));
+            const _Float16 z16 = __builtin_bit_cast(_Float16, uint16_t(0x6400u | sz[u % PB][t][1]));
+            ss[t] = h2{s16, s16};
+            zz[t] = h2{z16, z16};
+        }
+        load_b(u % PB, i + PB);
+        if (full || i < ng) {
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                v8h b[CB];
+#pragma unroll
+                for (int t = 0; t < CB; ++t)
+                    b[t] = st < 4 ? dequant_f16x8<false>(bw[t][st & 3].x, bw[t][st & 3].y, zz[t], ss[t])
+                                  : dequant_f16x8<true>(bw[t][st & 3].x, bw[t][st & 3].y, zz[t], ss[t]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const v8h a = __builtin_bit_cast(v8h, As[u & 1][8 * mt + st][lane]);
+#pragma unroll
+                    for (int t = 0; t < CB; ++t)
+                        acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[t], acc[mt][t], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    load_a(0);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) load_b(p, p);
+    stage_a(0);
+    load_a(1);
+    __syncthreads();
+    constexpr int U = 2;
+    int i0 = 0;
+    for (; i0 + U <= ng; i0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(i0 + u, u, true);
+    }
+    if (i0 < ng) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(i0 + u, u, false);
+    }
+
+    __syncthreads();
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw) + wave * (32 * 32 * CB);
+    const int n0w = 16 * nbw;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int t = 0; t < CB; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * q + (r & 3);
+                stage[row * (32 * CB) + 32 * t + j] = __half_as_ushort(__float2half_rn(acc[mt][t][r]));
+            }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2 * CB; ++u) {
+            const int kk = lane + 64 * u;
+            const int row = kk / (4 * CB);
+            const int ch = kk % (4 * CB);
+            const int m = m0 + 32 * mt + row;
+            const int n = n0w + 8 * ch;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (32 * CB) + 8 * ch);
+            if (m < M && n < N) *reinterpret_cast<uint4*>(y + int64_t(m) * N + n) = v;
+        }
+        __syncthreads();
+    }
+}
+
 // Compiled configurations: (MT, CB, PB, workgroups per CU, waves).
 #define QOQ_W8_CONFIGS(X)                                                                 \
     X(4, 2, 2, 2, 4) X(4, 2, 2, 1, 8) X(4, 1, 2, 1, 8) X(2, 2, 2, 2, 4) X(2, 1, 4, 2, 4)    \
     X(1, 1, 4, 3, 4) X(2, 1, 2, 2, 4)
 #define QOQ_W4A4_CONFIGS(X)                                                               \
     X(2, 1, 2, 2, 4) X(2, 1, 2, 1, 8) X(1, 1, 2, 3, 4) X(2, 2, 2, 2, 4)
+#define QOQ_W4A16_CONFIGS(X)                                                              \
+    X(2, 1, 2, 2, 4) X(2, 2, 2, 2, 4) X(4, 1, 2, 1, 8) X(1, 1, 2, 3, 4) X(4, 2, 2, 1, 8)
 
 template <int FMT>
 bool variant_config_exists(int mt, int cb, int pb, int minb, int nw) {
-    if (FMT == kFmtW8) {
+    if (FMT == kFmtW4A16) {
+#define X(a, b, c, d, e) if (mt == a && cb == b && pb == c && minb == d && nw == e) return true;
+        QOQ_W4A16_CONFIGS(X)
+#undef X
+    } else if (FMT == kFmtW8) {
 #define X(a, b, c, d, e) if (mt == a && cb == b && pb == c && minb == d && nw == e) return true;
         QOQ_W8_CONFIGS(X)
 #undef X
@@ -517,13 +775,16 @@ VariantPlan plan_variant(int fmt, int64_t M, int64_t N, int64_t K) {
     const bool w8 = fmt == kFmtW8;
     auto exists = [&](int a, int b, int c, int d, int e) {
         return w8 ? variant_config_exists<kFmtW8>(a, b, c, d, e)
-                  : variant_config_exists<kFmtW4A4>(a, b, c, d, e);
+                  : fmt == kFmtW4A16 ? variant_config_exists<kFmtW4A16>(a, b, c, d, e)
+                                     : variant_config_exists<kFmtW4A4>(a, b, c, d, e);
     };
     const GemmPlan g = plan_gemm(M, N, K);
     if (M <= 32) {
         p.mt = 1; p.cb = 1; p.pb = w8 ? 4 : 2; p.pa = 3; p.nw = 4;
     } else if (w8 && g.kind == 4 && exists(g.mt, g.cb, g.pd, g.pa, g.nw)) {
         p.mt = g.mt; p.cb = g.cb; p.pb = g.pd; p.pa = g.pa; p.nw = g.nw;
+    } else if (fmt == kFmtW4A16 && M > 256) {
+        p.mt = 4; p.cb = 1; p.pb = 2; p.pa = 1; p.nw = 8;
     } else if (!w8 && M > 256) {
         p.mt = 2; p.cb = 1; p.pb = 2; p.pa = 1; p.nw = 8;
     } else {
@@ -562,6 +823,29 @@ hipError_t launch_w8a8_pack(const float* W, int64_t N, int64_t K, uint8_t* packe
     const int64_t threads = N * K / 16;
     return launch_kernel(w8_pack_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
                          stream, W, (const uint16_t*)s, N, K, packed);
+}
+
+hipError_t launch_w4a16_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                             hipStream_t stream) {
+    const PackedLayout L = packed_layout(N, K);
+    const int64_t waves = N * L.ng;
+    return launch_kernel(w4a16_pack_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, stream,
+                         W, N, K, packed, packed + L.rec_offset, packed + L.rec_offset + L.rec_bytes,
+                         L.ng8);
+}
+
+hipError_t launch_w4a16_gemm(const VariantPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                             const uint8_t* packed, int64_t N, uint16_t* y, hipStream_t stream) {
+    const PackedLayout L = packed_layout(N, K);
+    const uint8_t* srec = packed + L.rec_offset;
+    const uint8_t* zrec = srec + L.rec_bytes;
+#define X(A, B, C, D, E)                                                                        \
+    if (p.mt == A && p.cb == B && p.pb == C && p.pa == D && p.nw == E)                              \
+        return launch_kernel(gemm_w4a16_kernel<A, B, C, D, E>, dim3(p.grid_x), dim3(64 * E), 0,     \
+                             stream, x, int(M), int(K), packed, srec, zrec, int(L.ng8), int(N), y);
+    QOQ_W4A16_CONFIGS(X)
+#undef X
+    return hipErrorInvalidConfiguration;
 }
 
 hipError_t launch_w4a4_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,

@@ -16,6 +16,9 @@
  *          s[n] = fp16(fp32(absmax / 127)); activations: qoq_quantize_act
  *          (per-token INT8, tile layout); y = fp16(acc * s_x[m] * s[n]) with
  *          the exact INT32 accumulator over all of K.
+ *   W4A16  weights: per (channel, group of 128) asymmetric UINT4 with an fp16
+ *          scale and a UINT4 zero, dequantized in the main loop to fp16;
+ *          activations fp16; fp16 MFMA, fp32 accumulation, fp16 y.
  *   W4A4   weights: per (channel, group of 128) symmetric INT4 in [-7, 7],
  *          fp16 scale fp16(fp32(absmax / 7)); activations: per (token,
  *          group) symmetric INT4, inv = fp32(7 / absmax), codes
@@ -60,6 +63,24 @@ qoq_status qoq_w8a8_pack_weights(const float* W, int64_t N, int64_t K, void* pac
 qoq_status qoq_w8a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
                          const void* packed, const uint16_t* s, int64_t N, uint16_t* y,
                          int32_t* acc_debug, void* stream);
+
+/* Bytes of the W4A16 packed weights: the W4A8 nibble layout holding the
+ * UINT4 codes q, then two regions of the W4A8 record shape holding, per
+ * (channel, group), the fp16 scale and the zero (uint16). 0 if invalid. */
+size_t qoq_w4a16_weight_bytes(int64_t N, int64_t K);
+
+/* W4A16 weight quantization and packing (W [N,K] fp32 -> packed): per
+ * (channel, group of 128) lo = min(0, min w), hi = max(0, max w),
+ * s = fp16(fp32(fp32(hi - lo) / 15)), z = clamp(rne(fp32(-lo / s)), 0, 15),
+ * q = clamp(rne(fp32(w / s)) + z, 0, 15). */
+qoq_status qoq_w4a16_pack_weights(const float* W, int64_t N, int64_t K, void* packed,
+                                  void* stream);
+
+/* W4A16 GEMM: x [M,K] fp16 row-major, weights dequantized to
+ * fp16((q - z) * s) in the main loop, fp16 MFMA with fp32 accumulation,
+ * y out [M,N] fp16. Requires N*K/2 and 2*M*K below 2^31 bytes. */
+qoq_status qoq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const void* packed, int64_t N,
+                          uint16_t* y, void* stream);
 
 /* Bytes of the W4A4 packed weights: the W4A8 packed layout's size; nibbles
  * hold u = code + 8 and each group's record slot holds its fp16 scale. */

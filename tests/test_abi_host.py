@@ -54,9 +54,22 @@ def test_variant_sizes_and_validation(monkeypatch):
     assert L.qoq_w4a4_gemm(P, 4, 4096, None, 4096, P, None) == NULL
     assert L.qoq_w4a4_quantize_act(P, 4, 200, P, None) == SHAPE
     assert L.qoq_w4a4_quantize_act(P + 2, 4, 256, P, None) == ALIGN
+    # W4A16: nibbles, then the scale records, then the zero records
+    assert L.qoq_w4a16_weight_bytes(4096, 4096) == 4096 * 2048 + 2 * (4096 // 16) * 4 * 256
+    assert L.qoq_w4a16_weight_bytes(16, 640) == 16 * 320 + 2 * 256
+    assert L.qoq_w4a16_weight_bytes(4008, 4096) == 0 and L.qoq_w4a16_weight_bytes(16, 100) == 0
+    assert L.qoq_w4a16_pack_weights(None, 16, 128, P, None) == NULL
+    assert L.qoq_w4a16_pack_weights(P, 16, 120, P, None) == SHAPE
+    assert L.qoq_w4a16_gemm(P, 4, 4096, P, 4008, P, None) == SHAPE
+    assert L.qoq_w4a16_gemm(P, -1, 4096, P, 4096, P, None) == SHAPE
+    assert L.qoq_w4a16_gemm(P, 4, 4096, P, 4096, None, None) == NULL
+    assert L.qoq_w4a16_gemm(P + 2, 4, 4096, P, 4096, P, None) == ALIGN
+    assert L.qoq_w4a16_gemm(P, 0, 4096, P, 4096, P, None) == OK
+    assert L.qoq_w4a16_gemm(P, 1 << 20, 1024, P, 4096, P, None) == SHAPE   # 2 M K = 2^31
     monkeypatch.setenv("QOQ_VARIANT_CONFIG", "9,9,9,9,9")
     assert L.qoq_w8a8_gemm(P, P, 4, 4096, P, P, 4096, P, None, None) == 8
     assert L.qoq_w4a4_gemm(P, 4, 4096, P, 4096, P, None) == 8
+    assert L.qoq_w4a16_gemm(P, 4, 4096, P, 4096, P, None) == 8
 
 
 def test_status_strings():

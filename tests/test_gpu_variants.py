@@ -1,8 +1,9 @@
 """The comparison GEMMs (W8A8 per-channel; W4A4 per-group with partial-sum
-scaling) against their oracle: codes and scales bit-exact (read through the
-documented layouts), W8A8 INT32 accumulators bit-exact, W8A8 fp16 output
-within the QoQ tolerance, W4A4 fp16 output within the error bound of its fp32
-accumulation over groups."""
+scaling; W4A16 weight-only) against their oracle: codes, scales and zeros
+bit-exact (read through the documented layouts), W8A8 INT32 accumulators
+bit-exact, W8A8 fp16 output within the QoQ tolerance, W4A4 and W4A16 fp16
+output within the error bound of their fp32 accumulation; the W4A16 in-loop
+dequantization bit-exact through one-hot activations."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import oracle
 import workloads as wl
 from act_layout import act_rows
-from variant_layout import w4_codes_scales, w8_codes, x4_codes_scales
+from variant_layout import w4_codes_scales, w4a16_codes_scales_zeros, w8_codes, x4_codes_scales
 
 qoq = pytest.importorskip("bit_integer_gemm_amd")
 
@@ -21,6 +22,7 @@ SHAPES = [(1, 128, 16), (5, 640, 208), (37, 384, 48), (64, 2048, 528), (100, 640
 W8_CONFIGS = ["4,2,2,2,4", "4,2,2,1,8", "4,1,2,1,8", "2,2,2,2,4", "2,1,4,2,4", "1,1,4,3,4",
               "2,1,2,2,4"]
 W4_CONFIGS = ["2,1,2,2,4", "2,1,2,1,8", "1,1,2,3,4", "2,2,2,2,4"]
+W16_CONFIGS = ["2,1,2,2,4", "2,2,2,2,4", "4,1,2,1,8", "1,1,2,3,4", "4,2,2,1,8"]
 
 
 def _half(X):
@@ -107,3 +109,66 @@ def test_w4a4_zero_groups(monkeypatch):
     tol = 2.0 ** -11 * np.abs(ref["y"]) + 6 * 2.0 ** -22 * ref["term_abs"] + 2.0 ** -24
     assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref["y"]) <= tol)
     assert torch.all(y[11] == 0)
+
+
+def _w16_check_weights(packed, ref, N, K):
+    q, sc, z = w4a16_codes_scales_zeros(packed.cpu().numpy(), N, K)
+    assert np.array_equal(q, ref["q"]), "weight codes"
+    assert np.array_equal(sc.view(np.uint16), ref["s"].view(np.uint16)), "weight scales"
+    assert np.array_equal(z, ref["z"]), "zeros"
+
+
+def _w16(M, K, N, monkeypatch, cfg=None, W=None, X=None):
+    if W is None:
+        W, X, _ = wl.make_inputs(M, K, N, seed=7 * M + K + N)
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    packed = qoq.w4a16_pack_weights(torch.from_numpy(W).to(DEV))
+    if cfg:
+        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+    print(f"\n[gpu-case] w4a16 cfg={cfg} M={M} K={K} N={N}", flush=True)
+    y = qoq.w4a16_gemm(_half(X), packed, N)
+    torch.cuda.synchronize()
+    ref = oracle.w4a16_linear(X, W)
+    _w16_check_weights(packed, ref, N, K)
+    # exact fp16 products summed in fp32 (K terms), then one fp16 rounding
+    yy = y.cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -11 * np.abs(ref["y"]) + (K + 2) * 2.0 ** -23 * ref["term_abs"] + 2.0 ** -24
+    bad = np.abs(yy - ref["y"]) > tol
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound, first at {np.argwhere(bad)[:3]}"
+    return y, ref
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w4a16_default(M, K, N, monkeypatch):
+    _w16(M, K, N, monkeypatch)
+
+
+@pytest.mark.parametrize("cfg", W16_CONFIGS)
+def test_w4a16_every_config(cfg, monkeypatch):
+    for (M, K, N) in [(37, 384, 48), (300, 1152, 528)]:
+        _w16(M, K, N, monkeypatch, cfg)
+
+
+@pytest.mark.parametrize("cfg", [None] + W16_CONFIGS)
+def test_w4a16_dequantization_exact(cfg, monkeypatch):
+    """One-hot rows select single weights: y[m, n] = w16[n, m] with nothing to
+    round, so the in-loop dequantization is compared bit for bit."""
+    K, N = 640, 208
+    M = K
+    W, _, _ = wl.make_inputs(1, K, N, seed=23)
+    X = np.eye(M, K, dtype=np.float16)
+    y, ref = _w16(M, K, N, monkeypatch, cfg, W=W, X=X)
+    assert np.array_equal(y.cpu().numpy(), ref["w16"].T), "dequantized weights differ"
+
+
+def test_w4a16_zero_groups_and_empty(monkeypatch):
+    W, X, _ = wl.make_inputs(20, 512, 64, seed=29)
+    W[3, 128:256] = 0
+    W[5] = 0
+    X[11] = 0
+    y, ref = _w16(20, 512, 64, monkeypatch, W=W, X=X)
+    assert torch.all(y[11] == 0) and torch.all(y[:, 5] == 0)
+    assert ref["s"][3, 1] == 0 and ref["z"][3, 1] == 0
+    packed = qoq.w4a16_pack_weights(torch.from_numpy(W).to(DEV))
+    e = qoq.w4a16_gemm(torch.empty((0, 512), dtype=torch.float16, device=DEV), packed, 64)
+    assert e.shape == (0, 64)

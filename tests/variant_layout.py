@@ -42,3 +42,24 @@ def x4_codes_scales(act, M, K):
     Mp = -(-M // 128) * 128
     s_a = a[off:off + (K // 128) * Mp * 4].view(np.float32).reshape(K // 128, Mp)[:, :M].T
     return codes, s_a
+
+
+def w4a16_codes_scales_zeros(packed, N, K):
+    """(q uint8 [N, K], s fp16 [N, K/128], z uint16 [N, K/128]) from the W4A16
+    packed weights: the W4A8 nibble layout with u = q, then the fp16 scales
+    and the zeros (uint16) in two regions of the record shape."""
+    p = np.asarray(packed)
+    ng = K // 128
+    nib = p[:N * K // 2].reshape(N // 16, ng, 4, 16, 16)     # nb, g, h, c, b
+    lo = nib & 15                                             # input 16h + b
+    hi = nib >> 4                                             # input 64 + 16h + b
+    q = np.concatenate([lo.transpose(0, 3, 1, 2, 4), hi.transpose(0, 3, 1, 2, 4)], axis=3)
+    q = q.reshape(N, K).astype(np.uint8)
+    ng8 = -(-ng // 8)
+    rb = N * ng8 * 16
+    recs = []
+    for r in range(2):
+        rec = p[N * K // 2 + r * rb:N * K // 2 + (r + 1) * rb].view(np.uint16)
+        rec = rec.reshape(N // 16, ng8, 16, 8).transpose(0, 2, 1, 3).reshape(N, ng8 * 8)
+        recs.append(rec[:, :ng])
+    return q, recs[0].view(np.float16), recs[1]

@@ -29,7 +29,7 @@ __all__ = [
     "LIB_PATH", "QoQError", "lib", "GROUP", "PACK_FROM_CANONICAL",
     "qoq_packed_weight_bytes", "qoq_act_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
     "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string", "qoq_w4a8_linear",
-    "qoq_linear_workspace_bytes",
+    "qoq_linear_workspace_bytes", "qoq_linear_path",
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
     "Workspace", "empty_act", "w4a8_linear",
     "w8a8_pack_weights", "w8a8_gemm", "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_gemm",
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.qoq_linear_workspace_bytes.restype = sz
         L.qoq_w4a8_linear.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.qoq_w4a8_linear.restype = ctypes.c_int
+        L.qoq_linear_path.argtypes = [i64, i64, i64]
+        L.qoq_linear_path.restype = ctypes.c_int
         # comparison GEMMs (include/qoq_variants.h)
         L.qoq_w8a8_weight_bytes.argtypes = [i64, i64]
         L.qoq_w8a8_weight_bytes.restype = sz
@@ -155,6 +157,11 @@ def qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
 
 def qoq_linear_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().qoq_linear_workspace_bytes(M, N, K))
+
+
+def qoq_linear_path(M: int, N: int, K: int) -> int:
+    """1 one fused launch, 0 quantizer then GEMM, -1 invalid."""
+    return int(lib().qoq_linear_path(M, N, K))
 
 
 def qoq_w4a8_linear(x, M, K, packed, s1, N, group, y, acc_debug, workspace, workspace_bytes,

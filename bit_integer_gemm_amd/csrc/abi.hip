@@ -111,6 +111,13 @@ size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return plan.valid ? size_t(plan.ws_bytes) : 0;
 }
 
+int qoq_linear_path(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return -1;
+    const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);
+    if (!plan.valid) return -1;
+    return plan.fused ? 1 : 0;
+}
+
 qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const void* packed,
                            const uint16_t* s1, int64_t N, int32_t group, uint16_t* y,
                            int32_t* acc_debug, void* workspace, size_t workspace_bytes,

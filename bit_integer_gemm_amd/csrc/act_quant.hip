@@ -12,23 +12,12 @@
 // 8 fp16 values per lane; the codes go out in the activation tile layout
 // (16-byte chunks of a row 256 bytes apart), 8 bytes per lane.
 #include "qoq_internal.hpp"
+#include "kernel_common.hpp"
 
 #include <hip/hip_fp16.h>
 
 namespace qoq {
 namespace {
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-    return __half2float(__ushort_as_half(uint16_t(bits16)));
-}
-
-__device__ __forceinline__ uint32_t quant_pair(uint32_t two_halves, float inv) {
-    const float a = rintf(h2f(two_halves & 0xffffu) * inv);
-    const float b = rintf(h2f(two_halves >> 16) * inv);
-    const int qa = int(fminf(fmaxf(a, -float(kActMax)), float(kActMax)));
-    const int qb = int(fminf(fmaxf(b, -float(kActMax)), float(kActMax)));
-    return (uint32_t(qa) & 0xffu) | ((uint32_t(qb) & 0xffu) << 8);
-}
 
 // Rows up to kRegK values are held in registers between the two passes (one
 // memory round trip); longer rows are re-read for the second pass.
@@ -73,7 +62,7 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mbits;
     __syncthreads();
     mbits = max(max(part[0], part[1]), max(part[2], part[3]));
-    const float a = h2f(mbits);
+    const float a = h2f(uint16_t(mbits));
     const float inv = a > 0.0f ? float(kActMax) / a : 0.0f;   // correctly rounded fp32
     if (threadIdx.x == 0) s_x[m] = a > 0.0f ? a / float(kActMax) : 0.0f;
     // pass 2: codes

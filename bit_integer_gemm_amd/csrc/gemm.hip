@@ -30,8 +30,13 @@ namespace {
 
 // Decode family (M <= 64): weight streaming.
 //
-// A workgroup owns CB column blocks (16 channels each) over the whole of K
-// and splits K between its KW waves in contiguous group ranges. Each wave
+// A workgroup owns 16*MT tokens x CB column blocks (16 channels each) over
+// the whole of K and splits K between its KW waves in contiguous group
+// ranges. With TM > 1 row tiles, the TM workgroups of one column range are
+// 8 workgroup ids apart, so they run on the same XCD (ids are dealt to the
+// XCDs round-robin) at the same time and the second read of the weights
+// hits that XCD's L2; splitting M halves the activation bytes each
+// workgroup pulls from L2, which bounds M = 64. Each wave
 // keeps PD groups of nibbles, records and activation fragments in flight
 // (register ring), so the HBM stream never waits on the MFMAs. The KW partial
 // INT32 accumulators are summed in LDS -- exact, so the result does not
@@ -42,7 +47,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
     const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_debug) {
+    int32_t* __restrict__ acc_debug, int TM) {
     static_assert(KW * MT * CB <= 64, "LDS reduction buffer above 64 KiB");
     __shared__ v4i red[KW * MT * CB * 64];
     const int lane = threadIdx.x & 63;
@@ -52,7 +57,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
     const int h = lane >> 4;
     const int ng = K >> 7;
     const int nbt = N >> 4;
-    const int nb0 = blockIdx.x * CB;
+    int tn = blockIdx.x, tm_id = 0;
+    if (TM > 1) {
+        const int q = blockIdx.x >> 3;
+        tm_id = q % TM;
+        tn = (q / TM) * 8 + (blockIdx.x & 7);
+    }
+    const int nb0 = tn * CB;
+    const int m0 = 16 * MT * tm_id;
     const int gpw = (ng + KW - 1) / KW;
     const int gb = min(ng, wave * gpw);
     const int cnt = min(ng, gb + gpw) - gb;
@@ -73,7 +85,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
     const int8_t* aptr[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        aptr[mt] = x8 + act_row_offset(min(16 * mt + c, M - 1), K) + kActUnit * h;
+        aptr[mt] = x8 + act_row_offset(min(m0 + 16 * mt + c, M - 1), K) + kActUnit * h;
 
     // Epilogue elements of this thread (see the end): their token and
     // channel scales are fetched now, so the epilogue waits for no load.
@@ -91,7 +103,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         const int hh = (t / CB) & 3;
         const int rr = ((t / CB) >> 2) & 3;
         const int mt = (t / CB) >> 4;
-        esx[it] = s_x[min(16 * mt + 4 * hh + rr, M - 1)];
+        esx[it] = s_x[min(m0 + 16 * mt + 4 * hh + rr, M - 1)];
         esw[it] = h2f(s1[16 * min(nb0 + cbi, nbt - 1) + cc]);
     }
 
@@ -213,7 +225,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
         const int hh = t & 3;
         const int rr = (t >> 2) & 3;
         const int mt = t >> 4;
-        const int m = 16 * mt + 4 * hh + rr;
+        const int m = m0 + 16 * mt + 4 * hh + rr;
         const int nbi = nb0 + cbi;
         if (m >= M || nbi >= nbt) continue;
         const int l = cc + 16 * hh;
@@ -929,7 +941,7 @@ template <int MT, int CB, int KW, int PD>
 hipError_t launch_decode(const GemmPlan& p, const Args& a, hipStream_t stream) {
     return launch_kernel(gemm_decode_kernel<MT, CB, KW, PD>, dim3(p.grid_x), dim3(64 * KW), 0,
                          stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
-                         a.acc_debug);
+                         a.acc_debug, p.grid_y);
 }
 
 template <int MT, int CB, int NW, int P>
@@ -1038,6 +1050,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         if (p.mt == 1) { p.cb = 1; p.kw = 8; p.pd = 4; }
         else if (p.mt == 2) { p.cb = 1; p.kw = 8; p.pd = 4; }
         else if (nbt >= 512) { p.cb = 2; p.kw = 4; p.pd = 2; }
+        else if (nbt % 16 == 0) { p.mt = 2; p.cb = 2; p.kw = 8; p.pd = 4; }   // two row tiles
         else { p.cb = 1; p.kw = 8; p.pd = 4; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
@@ -1070,7 +1083,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
             const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d,%d", fam, &a, &b, &c, &d, &e);
             const std::string f(fam);
             p.kind = -1;   // an override that names no compiled configuration is an error
-            if (f == "decode" && nf == 5 && M <= 16 * a && decode_config_exists(a, b, c, d)) {
+            if (f == "decode" && nf == 5 && M <= 64 && decode_config_exists(a, b, c, d)) {
                 p.kind = 1; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
             } else if (f == "lds" && nf == 5 && lds_config_exists(a, b, c, d)) {
                 p.kind = 2; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
@@ -1084,8 +1097,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         }
     }
     if (p.kind == 1) {
-        p.grid_x = int((nbt + p.cb - 1) / p.cb);
-        p.grid_y = 1;
+        // grid_y: row tiles, folded into the 1-D grid (the XCD pairing needs
+        // the column tiles in whole rounds of 8)
+        const int64_t tn = (nbt + p.cb - 1) / p.cb;
+        p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
+        if (p.grid_y > 1 && tn % 8 != 0) { p.kind = -1; return p; }
+        p.grid_x = int(tn * p.grid_y);
     } else if (p.kind == 4) {
         const int64_t tm = (M + 32 * p.mt - 1) / (32 * p.mt);
         const int64_t tn = (nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw);

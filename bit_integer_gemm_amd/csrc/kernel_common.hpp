@@ -1,7 +1,8 @@
 // Device helpers shared by the GEMM kernel families (W4A8 QoQ and the
-// comparison formats): operand vector types, the register-parallel UINT4
-// dequantization, the fp16 epilogue, group-record access and the XCD-aware
-// tile order.
+// comparison formats) and the activation quantizer: operand vector types,
+// the register-parallel UINT4 dequantization, the per-token activation
+// codes, the fp16 epilogue, group-record access and the XCD-aware tile
+// order.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -22,6 +23,16 @@ __device__ __forceinline__ int dequant4(uint32_t codes, uint32_t mul2, uint32_t 
 }
 
 __device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+// Per-token activation codes of two fp16 values (one 32-bit word) with the
+// row's fp32 inverse scale: clamp(rne(x * inv), -127, 127), two bytes.
+__device__ __forceinline__ uint32_t quant_pair(uint32_t two_halves, float inv) {
+    const float a = rintf(h2f(uint16_t(two_halves & 0xffffu)) * inv);
+    const float b = rintf(h2f(uint16_t(two_halves >> 16)) * inv);
+    const int qa = int(fminf(fmaxf(a, -127.0f), 127.0f));
+    const int qb = int(fminf(fmaxf(b, -127.0f), 127.0f));
+    return (uint32_t(qa) & 0xffu) | ((uint32_t(qb) & 0xffu) << 8);
+}
 
 __device__ __forceinline__ uint16_t epilogue_value(int32_t acc, float sx, float sw) {
     const float v = float(acc) * (sx * sw);

@@ -128,7 +128,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 // followed by the GEMM.
 struct LinearPlan {
     bool valid;         // false: QOQ_GEMM_CONFIG names no usable configuration
-    bool fused;
+    bool fused;         // one launch, every workgroup quantizes the tokens itself
     int kw;             // fused: waves splitting K
     int grid_x;
     int64_t x8_offset, sx_offset, gemm_ws_offset;   // workspace carve-up (two-call path)

@@ -179,6 +179,11 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
  * Host-only. */
 size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* How qoq_w4a8_linear runs this shape: 1 one fused launch (tokens
+ * quantized by every workgroup, no workspace), 0 the quantizer then the
+ * GEMM, -1 invalid shape or QOQ_GEMM_CONFIG. Host-only. */
+int qoq_linear_path(int64_t M, int64_t N, int64_t K);
+
 /* Per-token activation quantization and W4A8 GEMM in one call (run time).
  * Same result as qoq_quantize_act followed by qoq_w4a8_gemm, bit for bit
  * (codes, accumulators and y). For M <= 8 and K <= 8192 a single kernel

@@ -194,6 +194,19 @@ def test_linear_workspace_bytes():
     assert qoq.qoq_linear_workspace_bytes(4, 4000, 4096) == 0
 
 
+def test_linear_path(monkeypatch):
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    # one fused launch for M <= 8 with K <= 8192, otherwise two launches
+    assert [qoq.qoq_linear_path(M, 4096, 4096) for M in (1, 8, 9, 64, 256)] == [1, 1, 0, 0, 0]
+    assert qoq.qoq_linear_path(8, 4096, 16384) == 0
+    assert qoq.qoq_linear_path(0, 4096, 4096) == -1 and qoq.qoq_linear_path(4, 4008, 4096) == -1
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,16")
+    assert qoq.qoq_linear_path(16, 4096, 8192) == 1
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "decode,2,1,8,4")         # 2 row tiles, 13 column tiles
+    assert qoq.qoq_linear_path(64, 208, 4096) == -1
+    assert qoq.qoq_linear_path(64, 256, 4096) == 0
+
+
 def test_linear_rejects_bad_arguments(monkeypatch):
     monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
     f = qoq.qoq_w4a8_linear

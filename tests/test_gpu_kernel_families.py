@@ -82,6 +82,29 @@ def test_decode_family(monkeypatch, cfg):
             _run(monkeypatch, _fmt("decode", cfg), M, K, N)
 
 
+SPLIT = [c for c in DECODE if c[0] < 4]
+
+
+@pytest.mark.parametrize("cfg", SPLIT, ids=[_fmt("decode", c) for c in SPLIT])
+def test_decode_family_row_tiles(monkeypatch, cfg):
+    """More tokens than one workgroup's rows: 2 to 4 row tiles per column
+    range (the last one ragged), paired 8 workgroup ids apart."""
+    N = 16 * cfg[1] * 8 * 3
+    for M in (40, 64):
+        if M > 16 * cfg[0]:
+            _run(monkeypatch, _fmt("decode", cfg), M, 1152, N)
+
+
+def test_decode_row_tiles_need_whole_rounds(monkeypatch):
+    """Row tiles pair workgroups 8 ids apart, which needs the column tiles in
+    whole rounds of 8: otherwise the configuration is refused."""
+    pw, x8, s_x, _ = _case(*SHAPES_SMALL_M[2])          # M = 37, N = 48: 3 column tiles
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "decode,1,1,8,4")
+    with pytest.raises(qoq.QoQError) as e:
+        qoq.w4a8_gemm(x8, s_x, pw)
+    assert e.value.status == 8
+
+
 @pytest.mark.parametrize("cfg", LDS, ids=[_fmt("lds", c) for c in LDS])
 def test_shared_activation_family(monkeypatch, cfg):
     for (M, K, N) in SHAPES_SMALL_M + SHAPES_LARGE_M[:1]:

@@ -250,7 +250,7 @@ def main():
                  x8=qoq.empty_act(M, K, dev),
                  s_x=torch.empty(M, dtype=torch.float32, device=dev),
                  y=torch.empty((M, N), dtype=torch.float16, device=dev),
-                 fused=qoq.qoq_linear_workspace_bytes(M, N, K) == 0)
+                 fused=qoq.qoq_linear_path(M, N, K) == 1)
         c["act"] = ActCall(qoq, torch, c["x"], c["x8"], c["s_x"])
         per_m.append(c)
     # step j uses copies [n_m*j, n_m*j + n_m); each M is one qoq_w4a8_linear

@@ -100,6 +100,77 @@ def make_inputs(M, K, N, seed=0, outlier_frac=0.02, outlier_gain=20.0):
     return W, X, idx
 
 
+# ---------------------------------------------------------------------------
+# decode attention over a 4-bit KV cache
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AttnWorkload:
+    key: str
+    description: str
+    B: int            # sequences (one new query token each)
+    H: int            # query heads
+    H_kv: int         # key/value heads
+    D: int            # head dim
+    len_lo: int       # context lengths drawn uniformly in [len_lo, len_hi]
+    len_hi: int
+    key_outlier_frac: float = 0.02
+    key_outlier_gain: float = 10.0
+    seed: int = 0
+
+
+ATTN_WORKLOADS = {
+    "llama3_8b_attn": AttnWorkload(
+        "llama3_8b_attn", "Llama-3-8B decode attention (32 query / 8 KV heads, D=128), "
+        "64 sequences of 512-2048 tokens", 64, 32, 8, 128, 512, 2048),
+    "qwen15_72b_attn": AttnWorkload(
+        "qwen15_72b_attn", "Qwen1.5-72B decode attention (64 heads, D=128), "
+        "16 sequences of 512-2048 tokens", 16, 64, 64, 128, 512, 2048),
+    "llama3_8b_long": AttnWorkload(
+        "llama3_8b_long", "Llama-3-8B decode attention, 4 sequences of 8192-16384 tokens",
+        4, 32, 8, 128, 8192, 16384),
+}
+
+
+def make_attention(B, H, H_kv, D, lens, seed=0, key_outlier_frac=0.02, key_outlier_gain=10.0):
+    """(q [B,H,D], k [B,T,H_kv,D], v [B,T,H_kv,D]) float16 with T = max(lens):
+    N(0, 1) values; per KV head a fixed set of round(p*D) key channels scaled
+    by f (the key outlier channels smoothing targets). Draw order: the
+    outlier channels of every head, then k, v, q."""
+    rng = np.random.default_rng(seed)
+    T = int(max(lens)) if len(lens) else 0
+    n_out = int(round(key_outlier_frac * D))
+    idx = [rng.choice(D, n_out, replace=False) for _ in range(H_kv)]
+    k = rng.standard_normal((B, T, H_kv, D), dtype=np.float32)
+    for h in range(H_kv):
+        k[:, :, h, idx[h]] *= np.float32(key_outlier_gain)
+    k = k.astype(np.float16)
+    v = rng.standard_normal((B, T, H_kv, D), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((B, H, D), dtype=np.float32).astype(np.float16)
+    return q, k, v
+
+
+def attention_lens(w: AttnWorkload):
+    """Context lengths [B] int32, uniform in [len_lo, len_hi] (own stream)."""
+    rng = np.random.default_rng(w.seed + 1)
+    return rng.integers(w.len_lo, w.len_hi + 1, size=w.B).astype(np.int32)
+
+
+def make_attention_case(w: AttnWorkload):
+    lens = attention_lens(w)
+    q, k, v = make_attention(w.B, w.H, w.H_kv, w.D, lens, w.seed, w.key_outlier_frac,
+                             w.key_outlier_gain)
+    return q, k, v, lens
+
+
+def attention_bytes(lens, H, H_kv, D):
+    """HBM bytes one decode-attention call must move: per cached token and
+    KV head the 4-bit key and value codes (D/2 bytes each) with an fp16 scale
+    and a 4-bit zero apiece; the fp16 queries, outputs and smoothing factors."""
+    tokens = int(np.sum(lens))
+    B = len(lens)
+    return tokens * H_kv * (D + 5) + 2 * B * H * D * 2 + 2 * H_kv * D
+
+
 def algorithmic_bytes(M, K, N, group=GROUP):
     """HBM bytes the method must move for one GEMM (nibbles, group scale and
     zero at 1.5 B, fp16 channel scale, int8 activations, fp32 token scale,

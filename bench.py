@@ -62,7 +62,11 @@ def parse():
     p.add_argument("--shape-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the W8A8 / W4A4 comparison GEMMs")
+                   help="skip the W8A8 / W4A4 / W4A16 comparison GEMMs")
+    p.add_argument("--no-kv4", action="store_true",
+                   help="skip the KV4 decode-attention workloads")
+    p.add_argument("--kv4-workloads", default=",".join(KV4_WORKLOADS),
+                   help="comma list of KV4 decode-attention workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
 
@@ -397,6 +401,9 @@ def main():
 
     variants = None if args.no_variants else variant_comparison(torch, qoq, blocker, dev, ws,
                                                                 args.shape_iters)
+    kv4 = None if args.no_kv4 else kv4_attention_bench(torch, qoq, blocker, dev, ws,
+                                                       args.shape_iters,
+                                                       args.kv4_workloads.split(","))
     cpu = None if args.no_cpu_baseline else cpu_baseline(dw, shape, args.cpu_seconds)
     traffic = traffic_record()
 
@@ -439,10 +446,67 @@ def main():
         "copy_reference": copy_ref,
         "shapes": shapes_out,
         "variants": variants,
+        "kv4_attention": kv4,
         "host_cores": len(os.sched_getaffinity(0)),
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
+
+
+KV4_WORKLOADS = ("llama3_8b_attn", "qwen15_72b_attn", "llama3_8b_long")
+
+
+def kv4_attention_bench(torch, qoq, blocker, dev, ws, iters, keys=KV4_WORKLOADS):
+    """Decode attention over the 4-bit KV cache (SmoothAttention-scaled
+    queries), one call per workload: algorithmic bytes (4-bit codes with an
+    fp16 scale and a 4-bit zero per cached vector, queries, outputs) over the
+    mean launch time, against the HBM peak. The caches rotate over copies
+    totalling >= 512 MiB so every call reads from HBM."""
+    out = []
+    for key in keys:
+        w = wl.ATTN_WORKLOADS[key]
+        q, k, v, lens = wl.make_attention_case(w)
+        C = int(-(-int(lens.max()) // 32) * 32)
+        kd = torch.from_numpy(k.view(np.uint16)).view(torch.float16).to(dev)
+        vd = torch.from_numpy(v.view(np.uint16)).view(torch.float16).to(dev)
+        del k, v
+        lam = qoq.kv4_smooth_factors(kd[:4].reshape(-1, w.H_kv, w.D))
+        cache = qoq.kv4_alloc_cache(w.B, w.H_kv, C, dev)
+        qoq.kv4_append(kd, vd, lam, torch.zeros(w.B, dtype=torch.int32, device=dev), cache, C)
+        del kd, vd
+        n_copies = int(min(64, max(2, -(-ROTATE_BYTES // cache.numel()))))
+        caches = [cache] + [cache.clone() for _ in range(n_copies - 1)]
+        qd = torch.from_numpy(q.view(np.uint16)).view(torch.float16).to(dev)
+        lens_d = torch.from_numpy(lens).to(dev)
+        o = torch.empty_like(qd)
+        max_len = int(lens.max())
+        L = qoq.lib()
+        wsb = int(L.qoq_kv4_attention_workspace_bytes(w.B, w.H, w.H_kv, w.D, max_len))
+        wsp = None
+        if wsb:
+            buf = ws.get(wsb)
+            wsp, wsb = buf.data_ptr(), buf.numel()
+        st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+        calls = [lambda c=c: L.qoq_kv4_decode_attention(qd.data_ptr(), w.B, w.H, w.H_kv, w.D,
+                                                        lam.data_ptr(), c.data_ptr(), C,
+                                                        lens_d.data_ptr(), max_len, o.data_ptr(),
+                                                        wsp, wsb, st()) for c in caches]
+        for cl in calls[:2]:
+            rc = cl()
+            if rc:
+                raise RuntimeError(f"kv4 attention: {qoq.qoq_status_string(rc)}")
+        t = per_launch_times(torch, blocker, [calls], max(iters, len(calls)))[0]
+        b = wl.attention_bytes(lens, w.H, w.H_kv, w.D)
+        out.append(dict(workload=key, B=w.B, H=w.H, H_kv=w.H_kv, D=w.D,
+                        tokens=int(lens.sum()), max_len=max_len,
+                        splits=int(L.qoq_kv4_attention_workspace_bytes(w.B, w.H, w.H_kv, w.D, max_len)
+                                   // (w.B * w.H * 132 * 4)) or 1,
+                        us=round(t * 1e6, 2), bytes=b, gbs=round(b / t / 1e9, 1),
+                        hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                        fp16_kv_bytes=int(lens.sum()) * w.H_kv * w.D * 4))
+        del caches, cache, o
+        torch.cuda.empty_cache()
+    return out
 
 
 VARIANT_SHAPES = [("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),

@@ -3,6 +3,7 @@
 // synchronizes or prints.
 #include "qoq.h"
 #include "qoq_variants.h"
+#include "qoq_kv4.h"
 #include "qoq_internal.hpp"
 
 namespace {
@@ -263,6 +264,92 @@ qoq_status qoq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const void* p
     if (!plan.valid) return QOQ_ERR_CONFIG;
     const hipError_t e = qoq::launch_w4a16_gemm(plan, x, M, K, static_cast<const uint8_t*>(packed),
                                                 N, y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// KV4 decode attention
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kKv4MaxCapacity = int64_t(1) << 24;
+
+qoq_status check_kv4_heads(int64_t B, int64_t H, int64_t Hkv, int64_t D) {
+    if (D != 128 || B < 0 || B > kMaxDim || Hkv <= 0 || Hkv > 4096 || H <= 0 || H % Hkv != 0 ||
+        H / Hkv > 16)
+        return QOQ_ERR_SHAPE;
+    return QOQ_OK;
+}
+}  // namespace
+
+size_t qoq_kv4_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D) {
+    if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || B == 0) return 0;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return 0;
+    return size_t(qoq::kv4_cache_bytes(B, H_kv, capacity));
+}
+
+qoq_status qoq_kv4_smooth_factors(const uint16_t* k_calib, int64_t T, int64_t H_kv, int64_t D,
+                                  uint16_t* lambda, void* stream) {
+    if (check_kv4_heads(1, H_kv, H_kv, D) != QOQ_OK || T <= 0 || T > kMaxDim) return QOQ_ERR_SHAPE;
+    if (k_calib == nullptr || lambda == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(k_calib) || misaligned(lambda)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_kv4_smooth(k_calib, T, H_kv, lambda,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_kv4_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t T_new,
+                          int64_t H_kv, int64_t D, const uint16_t* lambda, const int32_t* start,
+                          void* cache, int64_t capacity, void* stream) {
+    if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || T_new < 0 || T_new > kKv4MaxCapacity)
+        return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (B == 0 || T_new == 0) return QOQ_OK;
+    if (B * T_new * H_kv > (int64_t(1) << 31) ||
+        B * H_kv * ((T_new + 31) / 32 + 1) * 512 > (int64_t(1) << 31))
+        return QOQ_ERR_SHAPE;
+    if (k == nullptr || v == nullptr || lambda == nullptr || start == nullptr || cache == nullptr)
+        return QOQ_ERR_NULL;
+    if (misaligned(k) || misaligned(v) || misaligned(lambda) || misaligned(cache))
+        return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_kv4_append(k, v, B, T_new, H_kv, lambda, start,
+                                                static_cast<uint8_t*>(cache), capacity,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+size_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t D,
+                                         int64_t max_len) {
+    if (check_kv4_heads(B, H, H_kv, D) != QOQ_OK || max_len < 0 || max_len > kKv4MaxCapacity)
+        return 0;
+    if (B == 0) return 0;
+    const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
+    return size_t(qoq::kv4_workspace_bytes(p, B, H));
+}
+
+qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int64_t H_kv,
+                                    int64_t D, const uint16_t* lambda, const void* cache,
+                                    int64_t capacity, const int32_t* lens, int64_t max_len,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    const qoq_status st = check_kv4_heads(B, H, H_kv, D);
+    if (st != QOQ_OK) return st;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (max_len < 0 || max_len > capacity) return QOQ_ERR_SHAPE;
+    if (B == 0) return QOQ_OK;
+    if (q == nullptr || lambda == nullptr || cache == nullptr || lens == nullptr || out == nullptr)
+        return QOQ_ERR_NULL;
+    if (misaligned(q) || misaligned(lambda) || misaligned(cache) || misaligned(out))
+        return QOQ_ERR_ALIGN;
+    const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
+    if (p.grid > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    const int64_t need = qoq::kv4_workspace_bytes(p, B, H);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < size_t(need)) return QOQ_ERR_WORKSPACE;
+        if (misaligned(workspace)) return QOQ_ERR_ALIGN;
+    }
+    const hipError_t e = qoq::launch_kv4_attention(
+        p, q, B, H, H_kv, lambda, static_cast<const uint8_t*>(cache), capacity, lens, max_len, out,
+        static_cast<float*>(need > 0 ? workspace : nullptr), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 

@@ -1,0 +1,575 @@
+// Decode attention over a 4-bit KV cache with SmoothAttention scaling.
+//
+// Pages: "QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+// Serving" (velog notes), sections "Insight" and "Methods / 1) Algorithm:
+// QoQ": the KV cache is held in 4 bits and SmoothAttention moves the
+// quantization difficulty of the keys onto the (unquantized) queries; the
+// QServe abstract: the fused attention is made memory-bound so the 4-bit
+// cache turns into throughput; "Part5 LLM部署技术" section 1.1 (the
+// SmoothQuant migration the smoothing factor follows) and section 3.
+//
+// Arithmetic (the readings the library and its oracle share):
+//   lambda[h, d] = fp16(sqrt(max_t |k[t, h, d]|)), 1 for an all-zero channel;
+//   a cached vector x (one token, one KV head, D = 128 values; keys are
+//   first divided by lambda in fp32) -> lo = min(0, min x), hi = max(0, max x),
+//   s = fp16((hi - lo) / 15), z = clamp(rne(-lo / s), 0, 15),
+//   code = clamp(rne(x / s) + z, 0, 15); it stands for (code - z) * s;
+//   q~ = fp16(q * lambda), scores q~ . k^ / sqrt(D), softmax, sum of p v^.
+//
+// Cache layout, per (sequence b, KV head h) region of C tokens (C a multiple
+// of 32), 133 C bytes: C/32 key blocks of 2 KiB, C/32 value blocks of 2 KiB,
+// then C/32 metadata blocks of 160 bytes. Everything is laid out in the lane
+// order of v_mfma_f32_16x16x32_f16, so every lane fetches its operands and
+// their scales with 16-byte loads and no address arithmetic in the loop:
+//   key block (32 tokens): 16 bytes at ((tile * 4 + g) * 16 + t) * 16 hold
+//     token 16 tile + t, dims 32 st + 8 g + e (word st, e = 0..7): byte b of
+//     a word holds dim e = b in the low nibble and e = b + 4 in the high one;
+//   value block (32 tokens): 4 bytes at ((g * 16 + d) * 8 + c) * 4 hold dim
+//     16 c + d of tokens pi(8 g + e), e = 0..7, same nibble order, where
+//     pi(8 g + e) = 4 g + e (e < 4), 16 + 4 g + e - 4 (e >= 4);
+//   metadata block (32 tokens): 32 fp16 s_k, 32 fp16 s_v and 32 bytes
+//     z_k | z_v << 4, each indexed by k = 8 g + e for token pi(k).
+// pi is the order in which the score MFMA leaves the tokens in the lanes
+// (lane (j, g) holds query j, tokens 4 g .. 4 g + 3 of each 16-token tile),
+// so the probabilities are already the B operand of the value MFMA.
+#include "qoq_internal.hpp"
+#include "kernel_common.hpp"
+
+#include <hip/hip_fp16.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
+namespace qoq {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kBlk = 32;                 // tokens per block
+constexpr int kBlkBytes = 2048;          // 32 tokens x 128 dims x 4 bits
+constexpr int kMetaBlkBytes = 160;       // per 32 tokens: 2 x 32 fp16 + 32 bytes
+constexpr int kRegionPerToken = kD + kMetaBlkBytes / kBlk;   // 133
+
+__device__ __forceinline__ int64_t region_offset(int64_t region, int64_t C) {
+    return region * C * kRegionPerToken;
+}
+
+// Per-vector UINT4 parameters of 64 lanes x 2 values (fp32); returns the
+// fp16 scale bits and the zero, identical in every lane.
+__device__ __forceinline__ void vec_params(float x0, float x1, uint16_t& sbits, int& z) {
+    float lo = fminf(0.0f, fminf(x0, x1)), hi = fmaxf(0.0f, fmaxf(x0, x1));
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    }
+    sbits = __half_as_ushort(__float2half_rn((hi - lo) / 15.0f));
+    const float sc = h2f(sbits);
+    z = sc != 0.0f ? int(fminf(fmaxf(rintf(-lo / sc), 0.0f), 15.0f)) : 0;
+}
+
+__device__ __forceinline__ int vec_code(float x, float sc, int z) {
+    return sc != 0.0f ? min(15, max(0, int(rintf(x / sc)) + z)) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// smoothing factors: one workgroup per 64 channels, 4 row phases
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) kv4_smooth_kernel(const uint16_t* __restrict__ k, int64_t T,
+                                                         int cols, uint16_t* __restrict__ lam) {
+    const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int ph = threadIdx.x >> 6;
+    uint32_t m = 0;
+    if (col < cols)
+        for (int64_t t = ph; t < T; t += 4) m = max(m, uint32_t(k[t * cols + col]) & 0x7fffu);
+    __shared__ uint32_t part[4][64];
+    part[ph][threadIdx.x & 63] = m;
+    __syncthreads();
+    if (ph == 0 && col < cols) {
+        m = max(max(part[0][threadIdx.x], part[1][threadIdx.x]),
+                max(part[2][threadIdx.x], part[3][threadIdx.x]));
+        const float a = h2f(uint16_t(m));
+        lam[col] = a > 0.0f ? __half_as_ushort(__float2half_rn(sqrtf(a))) : uint16_t(0x3c00);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// append: keys (smoothed) and metadata; one wave per (sequence, new token,
+// KV head), lane l holds dims 2l, 2l + 1
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) kv4_append_keys_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B, int Tn, int Hkv,
+    const uint16_t* __restrict__ lam, const int32_t* __restrict__ start, uint8_t* __restrict__ cache,
+    int64_t C) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (w >= int64_t(B) * Tn * Hkv) return;
+    const int h = int(w % Hkv);
+    const int i = int((w / Hkv) % Tn);
+    const int b = int(w / (int64_t(Hkv) * Tn));
+    const int64_t pos = int64_t(max(start[b], 0)) + i;
+    if (pos >= C) return;
+    const int64_t src = ((int64_t(b) * Tn + i) * Hkv + h) * kD + 2 * lane;
+    const uint32_t kk = *reinterpret_cast<const uint32_t*>(k + src);
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + src);
+    const uint32_t ll = *reinterpret_cast<const uint32_t*>(lam + h * kD + 2 * lane);
+    const float k0 = h2f(uint16_t(kk & 0xffffu)) / h2f(uint16_t(ll & 0xffffu));
+    const float k1 = h2f(uint16_t(kk >> 16)) / h2f(uint16_t(ll >> 16));
+    const float v0 = h2f(uint16_t(vv & 0xffffu)), v1 = h2f(uint16_t(vv >> 16));
+    uint16_t sk, sv;
+    int zk, zv;
+    vec_params(k0, k1, sk, zk);
+    vec_params(v0, v1, sv, zv);
+    const float fk = h2f(sk);
+    const int c0 = vec_code(k0, fk, zk), c1 = vec_code(k1, fk, zk);
+    // word wi = lane / 4 holds dims 8 wi + e; lane 4wi + r holds e = 2r, 2r + 1;
+    // byte b of the word = code(e = b) | code(e = b + 4) << 4
+    const int up = __shfl_down(c0 | (c1 << 8), 2, 64);     // lanes 4wi+2, 4wi+3 -> 4wi, 4wi+1
+    const uint32_t half16 = uint32_t(c0 | ((up & 0xff) << 4)) | (uint32_t(c1 | (((up >> 8) & 0xff) << 4)) << 8);
+    const uint32_t hi16 = __shfl_down(half16, 1, 64);
+    uint8_t* region = cache + region_offset(int64_t(b) * Hkv + h, C);
+    const int64_t blk = pos / kBlk;
+    const int tt = int(pos % kBlk);
+    if ((lane & 3) == 0) {
+        const int wi = lane >> 2;
+        const int st = wi >> 2, g = wi & 3;
+        const int64_t off = blk * kBlkBytes + ((tt >> 4) * 4 + g) * 256 + (tt & 15) * 16 + 4 * st;
+        *reinterpret_cast<uint32_t*>(region + off) = (half16 & 0xffffu) | (hi16 << 16);
+    }
+    if (lane < 3) {
+        // k-index of the token in its block: lane group g = (tt % 16) / 4,
+        // e = tt % 4 + 4 (tt / 16)
+        const int kk = 8 * ((tt & 15) >> 2) + (tt & 3) + 4 * (tt >> 4);
+        uint8_t* meta = region + (C / kBlk) * 2 * kBlkBytes + blk * kMetaBlkBytes;
+        if (lane < 2) reinterpret_cast<uint16_t*>(meta)[lane * 32 + kk] = lane == 0 ? sk : sv;
+        else meta[128 + kk] = uint8_t(zk | (zv << 4));
+    }
+}
+
+// append: value codes. One thread per 4-byte word (g, d, c) of every block
+// the new tokens touch; it rewrites the nibbles of the new tokens and keeps
+// the others (tokens of one word may arrive in different calls).
+__global__ void __launch_bounds__(256) kv4_append_values_kernel(
+    const uint16_t* __restrict__ v, int B, int Tn, int Hkv, const int32_t* __restrict__ start,
+    uint8_t* __restrict__ cache, int64_t C, int nblk_touch) {
+    const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t per_region = int64_t(nblk_touch) * 512;
+    if (gid >= int64_t(B) * Hkv * per_region) return;
+    const int64_t region = gid / per_region;
+    const int b = int(region / Hkv), h = int(region % Hkv);
+    const int rem = int(gid % per_region);
+    const int64_t s0 = max(start[b], 0);
+    const int64_t blk = s0 / kBlk + rem / 512;
+    const int word = rem % 512;
+    const int g = word >> 7, d = (word >> 3) & 15, c = word & 7;
+    if (blk >= C / kBlk) return;
+    uint8_t* rg = cache + region_offset(region, C);
+    uint32_t* wp = reinterpret_cast<uint32_t*>(rg + (C / kBlk) * kBlkBytes + blk * kBlkBytes + word * 4);
+    const uint8_t* meta = rg + (C / kBlk) * 2 * kBlkBytes + blk * kMetaBlkBytes;
+    uint32_t wv = *wp;
+    bool any = false;
+    for (int e = 0; e < 8; ++e) {
+        const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+        const int64_t pos = blk * kBlk + tok;
+        const int64_t i = pos - s0;
+        if (i < 0 || i >= Tn || pos >= C) continue;
+        const float sc = h2f(reinterpret_cast<const uint16_t*>(meta)[32 + 8 * g + e]);
+        const int z = int(meta[128 + 8 * g + e] >> 4);
+        const float x = h2f(v[((int64_t(b) * Tn + i) * Hkv + h) * kD + 16 * c + d]);
+        const uint32_t code = uint32_t(vec_code(x, sc, z));
+        const int sh = 8 * (e & 3) + 4 * (e >> 2);
+        wv = (wv & ~(0xfu << sh)) | (code << sh);
+        any = true;
+    }
+    if (any) *wp = wv;
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+// Eight nibbles of a word (byte b: e = b low, e = b + 4 high) -> fp16 pairs
+// of 1024 + code in e order. The byte permute takes the 0x64 exponent bytes
+// from c64 = 0x64646464, so one AND finishes each pair.
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t c64, h2 (&r)[4]) {
+    const uint32_t w4 = w >> 4;
+    r[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w, 0x04010400u) & 0xff0fff0fu);
+    r[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w, 0x04030402u) & 0xff0fff0fu);
+    r[2] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w4, 0x04010400u) & 0xff0fff0fu);
+    r[3] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w4, 0x04030402u) & 0xff0fff0fu);
+}
+
+__device__ __forceinline__ v8h join(const h2 (&r)[4]) {
+    v8h o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = r[i][0];
+        o[2 * i + 1] = r[i][1];
+    }
+    return o;
+}
+
+struct AttnArgs {
+    const uint16_t* q;         // [B, H, D]
+    const uint16_t* lam;       // [Hkv, D]
+    const uint8_t* cache;
+    const int32_t* lens;       // [B]
+    uint16_t* out;             // [B, H, D]
+    float* part;               // [B, H, splits, D + 2] when splits > 1
+    int64_t C;
+    int B, H, Hkv, G, splits, bps, max_len;
+};
+
+// One workgroup (4 waves) per (sequence, KV head, split). Wave w takes the
+// split's blocks w, w + 4, ...; per block: 2 score MFMAs tiles x 4 steps
+// (tokens x queries), online softmax per query, 8 value MFMAs (dims x
+// queries). The four waves' states are merged in LDS at the end.
+__global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15;          // query of the group (MFMA column)
+    const int g = lane >> 4;          // lane group
+    const int sp = blockIdx.x % a.splits;
+    const int region = blockIdx.x / a.splits;
+    const int h = region % a.Hkv;
+    const int b = region / a.Hkv;
+    const int64_t C = a.C;
+    const int len = int(min(int64_t(max(min(a.lens[b], a.max_len), 0)), C));
+    const int nb = (len + kBlk - 1) / kBlk;
+    const int blk0 = sp * a.bps;
+    const int blk1 = min(nb, blk0 + a.bps);
+    // a split past the end of its context writes nothing: the merge of the
+    // splits reads only those that hold tokens
+    if (a.splits > 1 && blk0 >= nb) return;
+    const uint8_t* rg = a.cache + region_offset(region, C);
+    const uint8_t* kbase = rg;
+    const uint8_t* vbase = rg + (C / kBlk) * kBlkBytes;
+    const uint8_t* mbase = rg + (C / kBlk) * 2 * kBlkBytes;
+    const bool qvalid = j < a.G;
+    const int qh = h * a.G + min(j, a.G - 1);
+
+    // smoothed query operand: lane (j, g), step st holds dims 32 st + 8 g + e
+    v8h qop[4];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int d0 = 32 * st + 8 * g;
+        const uint4 qq = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + qh) * kD + d0);
+        const uint4 ll = *reinterpret_cast<const uint4*>(a.lam + h * kD + d0);
+        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w}, lw[4] = {ll.x, ll.y, ll.z, ll.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const float x = h2f(uint16_t(qw[i] >> (16 * hf))) * h2f(uint16_t(lw[i] >> (16 * hf)));
+                const _Float16 xs = qvalid ? static_cast<_Float16>(x) : _Float16(0.0f);
+                qop[st][2 * i + hf] = xs;
+                qsum += float(xs);
+            }
+        }
+    }
+    qsum += __shfl_xor(qsum, 16, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+    // scores in the log2 domain: log2(e) / sqrt(D)
+    const float kScale = 1.4426950408889634f * 0.08838834764831845f;
+
+    float m = -INFINITY, l = 0.0f;
+    v4f o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto kofs = [&](int tile) { return (tile * 4 + g) * 256 + j * 16; };
+    const int vofs = (g * 16 + j) * 32;
+    // per block: key codes (2 tiles), value codes, and the lane's 8 entries
+    // of each metadata array (s_k, s_v, zero bytes)
+    struct Blk {
+        uint4 k0, k1, v0, v1, sk, sv;
+        uint2 z;
+    };
+    auto load = [&](Blk& r, int blk) {
+        const uint8_t* kb = kbase + int64_t(blk) * kBlkBytes;
+        const uint8_t* vb = vbase + int64_t(blk) * kBlkBytes;
+        const uint8_t* mb = mbase + int64_t(blk) * kMetaBlkBytes;
+        r.k0 = *reinterpret_cast<const uint4*>(kb + kofs(0));
+        r.k1 = *reinterpret_cast<const uint4*>(kb + kofs(1));
+        r.v0 = *reinterpret_cast<const uint4*>(vb + vofs);
+        r.v1 = *reinterpret_cast<const uint4*>(vb + vofs + 16);
+        r.sk = *reinterpret_cast<const uint4*>(mb + 16 * g);
+        r.sv = *reinterpret_cast<const uint4*>(mb + 64 + 16 * g);
+        r.z = *reinterpret_cast<const uint2*>(mb + 128 + 8 * g);
+    };
+    const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
+    auto compute = [&](const Blk& r, int blk) {
+        const int tbase = blk * kBlk;
+        auto valid = [&](int e) {
+            const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+            return tbase + tok < len;
+        };
+        const uint32_t skw[4] = {r.sk.x, r.sk.y, r.sk.z, r.sk.w};
+        // zero bytes z_k | z_v << 4 of the lane's tokens e = 0..3, 4..7
+        const uint32_t zk03 = r.z.x & 0x0f0f0f0fu, zk47 = r.z.y & 0x0f0f0f0fu;
+        const uint32_t zv03 = (r.z.x >> 4) & 0x0f0f0f0fu, zv47 = (r.z.y >> 4) & 0x0f0f0f0fu;
+        // scores: S[token, query] = q~ . u (u exact small integers)
+        float zs[8];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint4 kt = tile ? r.k1 : r.k0;
+            const uint32_t kw[4] = {kt.x, kt.y, kt.z, kt.w};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                h2 u[4];
+                unpack8(kw[st], c64, u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = u[i] - h2{_Float16(1024.0f), _Float16(1024.0f)};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), qop[st], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * tile + i;
+                const h2 sk2 = __builtin_bit_cast(h2, skw[e >> 1]);
+                const float zk = float(((tile ? zk47 : zk03) >> (8 * i)) & 0xffu);
+                const float sc = (acc[i] - zk * qsum) * (float(sk2[e & 1]) * kScale);
+                zs[e] = valid(e) ? sc : -INFINITY;
+            }
+        }
+        // online softmax for query j over the block's 32 tokens; the
+        // accumulators are rescaled only when the running maximum grows by
+        // more than 2^8 (probabilities stay below 256 in between)
+        float bm = zs[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zs[e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const bool grow = bm > m + 8.0f;
+        if (__ballot(grow) != 0) {
+            const float fac = grow ? __builtin_amdgcn_exp2f(m - bm) : 1.0f;
+            l *= fac;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c] = o[c] * fac;
+            m = grow ? bm : m;
+        }
+        v8h pop;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(zs[e] - m);
+            l += pe;
+            pop[e] = static_cast<_Float16>(pe);
+        }
+        // values: (1024 + u) - (1024 + z) = u - z exactly, times s (one
+        // rounding); tokens past the context get scale 0 and a neutral zero
+        h2 zz[4], ss[4];
+        const uint32_t svw[4] = {r.sv.x, r.sv.y, r.sv.z, r.sv.w};
+        // 1024 + z_v pairs: the zero bytes with 0x64 exponent bytes between
+        const uint32_t zvw[4] = {__builtin_amdgcn_perm(c64, zv03, 0x04010400u),
+                                 __builtin_amdgcn_perm(c64, zv03, 0x04030402u),
+                                 __builtin_amdgcn_perm(c64, zv47, 0x04010400u),
+                                 __builtin_amdgcn_perm(c64, zv47, 0x04030402u)};
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            const uint32_t keep = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
+            ss[pr] = __builtin_bit_cast(h2, svw[pr] & keep);
+            zz[pr] = __builtin_bit_cast(h2, (zvw[pr] & keep) | (0x64006400u & ~keep));
+        }
+        const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            h2 u[4];
+            unpack8(vw[c], c64, u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u[i] = (u[i] - zz[i]) * ss[i];
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pop, o[c], 0, 0, 0);
+        }
+    };
+
+    // the wave's blocks: blk0 + wave, + 4, ...; the next block's loads are
+    // in flight while one is computed
+    Blk cur, nxt;
+    int bi = blk0 + wave;
+    if (bi < blk1) load(cur, bi);
+    for (; bi < blk1; bi += 4) {
+        if (bi + 4 < blk1) load(nxt, bi + 4);
+        compute(cur, bi);
+        cur = nxt;
+    }
+
+    // merge the four waves: lane (j, g) holds query j, dims 16 c + 4 g + i
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    __shared__ float sm[4][16], sl[4][16];
+    __shared__ float so[4][16][kD + 4];
+    if (g == 0) {
+        sm[wave][j] = m;
+        sl[wave][j] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[wave][j][16 * c + 4 * g + i] = o[c][i];
+    __syncthreads();
+    // thread -> (query jq, 8 dims); 16 queries x 128 dims / 256 threads
+    const int jq = threadIdx.x >> 4;
+    const int d0 = (threadIdx.x & 15) * 8;
+    if (jq >= a.G) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][jq]);
+    float L = 0.0f, f[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f[w] = M == -INFINITY ? 0.0f : exp2f(sm[w][jq] - M);
+        L += f[w] * sl[w][jq];
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[e] += f[w] * so[w][jq][d0 + e];
+    }
+    const int64_t row = int64_t(b) * a.H + h * a.G + jq;
+    if (a.splits == 1) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = L > 0.0f ? acc[2 * e] / L : 0.0f;
+            const float x1 = L > 0.0f ? acc[2 * e + 1] / L : 0.0f;
+            pk[e] = uint32_t(__half_as_ushort(__float2half_rn(x0))) |
+                    (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+        }
+        *reinterpret_cast<uint4*>(a.out + row * kD + d0) = uint4{pk[0], pk[1], pk[2], pk[3]};
+    } else {
+        float* pp = a.part + (row * a.splits + sp) * (kD + 4);
+        *reinterpret_cast<float4*>(pp + d0) = float4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<float4*>(pp + d0 + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+        if (d0 == 0) {
+            pp[kD] = M;
+            pp[kD + 1] = L;
+        }
+    }
+}
+
+// Splits of one (sequence, query head) merged: one wave, 2 dims per lane;
+// only the splits that hold tokens of the sequence are read. Lane s reads
+// split s's maximum and sum (one round trip for all splits), the weights
+// come from wave reductions, and the partial outputs are read eight splits
+// at a time with independent loads.
+__global__ void __launch_bounds__(256) kv4_combine_kernel(const float* __restrict__ part, int rows,
+                                                          int H, int splits, int bps,
+                                                          const int32_t* __restrict__ lens,
+                                                          int max_len, int64_t C,
+                                                          uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int b = row / H;
+    const int len = int(min(int64_t(max(min(lens[b], max_len), 0)), C));
+    const int nb = (len + kBlk - 1) / kBlk;
+    const int ns = min(splits, (nb + bps - 1) / bps);
+    const float* pp = part + int64_t(row) * splits * (kD + 4);
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 64)
+        if (s0 + lane < ns) M = fmaxf(M, pp[int64_t(s0 + lane) * (kD + 4) + kD]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        float f = 0.0f, ls = 0.0f;
+        if (s0 + lane < ns) {
+            const float* q = pp + int64_t(s0 + lane) * (kD + 4);
+            f = exp2f(q[kD] - M);
+            ls = f * q[kD + 1];
+        }
+        for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off, 64);
+        L += ls;
+        const int n = min(64, ns - s0);
+        for (int s1 = 0; s1 < n; s1 += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int ss = min(s1 + u, n - 1);
+                v[u] = *reinterpret_cast<const float2*>(pp + int64_t(s0 + ss) * (kD + 4) + 2 * lane);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float fu = __shfl(f, s1 + u, 64);
+                if (s1 + u < n) {
+                    o0 += fu * v[u].x;
+                    o1 += fu * v[u].y;
+                }
+            }
+        }
+    }
+    const float x0 = L > 0.0f ? o0 / L : 0.0f, x1 = L > 0.0f ? o1 / L : 0.0f;
+    *reinterpret_cast<uint32_t*>(out + int64_t(row) * kD + 2 * lane) =
+        uint32_t(__half_as_ushort(__float2half_rn(x0))) | (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+}
+
+}  // namespace
+
+int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C) { return B * Hkv * C * kRegionPerToken; }
+
+// One workgroup per (sequence, KV head) when that gives ~512 workgroups
+// (two rounds of 4-wave workgroups over the 256 CUs); fewer, longer
+// contexts are cut into equal splits, at least one block per wave, merged by
+// a second kernel. (Measured on MI355X: cutting every context into fixed
+// 256-1024-token splits to even out ragged lengths is slower -- the
+// per-workgroup query set-up and merge cost more than the imbalance.)
+// QOQ_KV4_SPLITS=<n> forces n splits.
+Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
+    Kv4Plan p{};
+    const int64_t nb = std::max<int64_t>(1, (max_len + kBlk - 1) / kBlk);
+    const int64_t regions = std::max<int64_t>(1, B * Hkv);
+    int64_t splits = (512 + regions - 1) / regions;
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (nb + 3) / 4));
+    if (const char* env = std::getenv("QOQ_KV4_SPLITS")) {
+        const int v = std::atoi(env);
+        if (v > 0) splits = v;
+    }
+    p.splits = int(splits);
+    p.bps = int(std::max<int64_t>(1, (nb + splits - 1) / splits));
+    p.grid = B * Hkv * splits;
+    return p;
+}
+
+hipError_t launch_kv4_smooth(const uint16_t* k, int64_t T, int64_t Hkv, uint16_t* lam,
+                             hipStream_t stream) {
+    const int cols = int(Hkv * kD);
+    return launch_kernel(kv4_smooth_kernel, dim3(unsigned((cols + 63) / 64)), dim3(256), 0, stream,
+                         k, T, cols, lam);
+}
+
+hipError_t launch_kv4_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t Tn,
+                             int64_t Hkv, const uint16_t* lam, const int32_t* start, uint8_t* cache,
+                             int64_t C, hipStream_t stream) {
+    const int64_t waves = B * Tn * Hkv;
+    hipError_t e = launch_kernel(kv4_append_keys_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0,
+                                 stream, k, v, int(B), int(Tn), int(Hkv), lam, start, cache, C);
+    if (e != hipSuccess) return e;
+    // blocks a run of Tn tokens can touch from any start
+    const int nblk_touch = int((Tn + kBlk - 1) / kBlk + 1);
+    const int64_t threads = B * Hkv * int64_t(nblk_touch) * 512;
+    return launch_kernel(kv4_append_values_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
+                         stream, v, int(B), int(Tn), int(Hkv), start, cache, C, nblk_touch);
+}
+
+int64_t kv4_workspace_bytes(const Kv4Plan& p, int64_t B, int64_t H) {
+    return p.splits > 1 ? B * H * p.splits * (kD + 4) * int64_t(sizeof(float)) : 0;
+}
+
+hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,
+                                int64_t Hkv, const uint16_t* lam, const uint8_t* cache, int64_t C,
+                                const int32_t* lens, int64_t max_len, uint16_t* out, float* part,
+                                hipStream_t stream) {
+    AttnArgs a{q, lam, cache, lens, out, part, C, int(B), int(H), int(Hkv), int(H / Hkv), p.splits,
+               p.bps, int(max_len)};
+    hipError_t e = launch_kernel(kv4_attention_kernel, dim3(unsigned(p.grid)), dim3(256), 0, stream, a);
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int rows = int(B * H);
+    return launch_kernel(kv4_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,
+                         (const float*)part, rows, int(H), p.splits, p.bps, lens, int(max_len), C,
+                         out);
+}
+
+}  // namespace qoq

@@ -177,6 +177,25 @@ hipError_t launch_w8a8_gemm(const VariantPlan& p, const int8_t* x8, const float*
                             uint16_t* y, int32_t* acc_debug, hipStream_t stream);
 hipError_t launch_w4a4_gemm(const VariantPlan& p, const uint8_t* act, int64_t M, int64_t K,
                             const uint8_t* packed, int64_t N, uint16_t* y, hipStream_t stream);
+// KV4 decode attention (4-bit KV cache, SmoothAttention scaling)
+struct Kv4Plan {
+    int splits;        // workgroups per (sequence, KV head), context split evenly
+    int bps;           // 32-token blocks per split
+    int64_t grid;
+};
+int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C);
+Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len);
+hipError_t launch_kv4_smooth(const uint16_t* k, int64_t T, int64_t Hkv, uint16_t* lam,
+                             hipStream_t stream);
+hipError_t launch_kv4_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t Tn,
+                             int64_t Hkv, const uint16_t* lam, const int32_t* start, uint8_t* cache,
+                             int64_t C, hipStream_t stream);
+int64_t kv4_workspace_bytes(const Kv4Plan& p, int64_t B, int64_t H);
+hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,
+                                int64_t Hkv, const uint16_t* lam, const uint8_t* cache, int64_t C,
+                                const int32_t* lens, int64_t max_len, uint16_t* out, float* part,
+                                hipStream_t stream);
+
 hipError_t launch_linear_fused(const LinearPlan& plan, const uint16_t* x, int64_t M, int64_t K,
                                const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
                                int32_t* acc_debug, hipStream_t stream);

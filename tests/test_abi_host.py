@@ -72,6 +72,45 @@ def test_variant_sizes_and_validation(monkeypatch):
     assert L.qoq_w4a16_gemm(P, 4, 4096, P, 4096, P, None) == 8
 
 
+def test_kv4_sizes_and_validation(monkeypatch):
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    L = qoq.lib()
+    assert L.qoq_kv4_cache_bytes(64, 8, 2048, 128) == 64 * 8 * 2048 * 133
+    assert L.qoq_kv4_cache_bytes(2, 8, 100, 128) == 0          # capacity not a multiple of 32
+    assert L.qoq_kv4_cache_bytes(2, 8, 64, 64) == 0            # head dim other than 128
+    assert L.qoq_kv4_cache_bytes(0, 8, 64, 128) == 0
+    # one workgroup per (sequence, KV head) when there are 512 of them: no
+    # workspace; few long contexts are split (here 16 ways) and their partial
+    # results (132 floats per query head and split) meet in the workspace
+    assert L.qoq_kv4_attention_workspace_bytes(64, 32, 8, 128, 2048) == 0
+    assert L.qoq_kv4_attention_workspace_bytes(4, 32, 8, 128, 16384) == 4 * 32 * 16 * 132 * 4
+    monkeypatch.setenv("QOQ_KV4_SPLITS", "3")
+    assert L.qoq_kv4_attention_workspace_bytes(4, 32, 8, 128, 16384) == 4 * 32 * 3 * 132 * 4
+    monkeypatch.delenv("QOQ_KV4_SPLITS")
+    att = L.qoq_kv4_decode_attention
+    assert att(P, 2, 32, 8, 64, P, P, 64, P, 64, P, None, 0, None) == SHAPE      # D
+    assert att(P, 2, 30, 8, 128, P, P, 64, P, 64, P, None, 0, None) == SHAPE     # H % H_kv
+    assert att(P, 2, 64, 2, 128, P, P, 64, P, 64, P, None, 0, None) == SHAPE     # group of 32
+    assert att(P, 2, 32, 8, 128, P, P, 64, P, 65, P, None, 0, None) == SHAPE     # max_len > capacity
+    assert att(P, 2, 32, 8, 128, P, P, 60, P, 32, P, None, 0, None) == SHAPE     # capacity % 32
+    assert att(P, 0, 32, 8, 128, None, None, 64, None, 64, None, None, 0, None) == OK
+    assert att(None, 2, 32, 8, 128, P, P, 64, P, 64, P, None, 0, None) == NULL
+    assert att(P, 2, 32, 8, 128, P, P, 64, None, 64, P, None, 0, None) == NULL
+    assert att(P + 2, 2, 32, 8, 128, P, P, 64, P, 64, P, None, 0, None) == ALIGN
+    assert att(P, 4, 32, 8, 128, P, P, 16384, P, 16384, P, None, 0, None) == WORKSPACE
+    assert att(P, 4, 32, 8, 128, P, P, 16384, P, 16384, P, P, 1024, None) == WORKSPACE
+    app = L.qoq_kv4_append
+    assert app(P, P, 2, 0, 8, 128, P, P, P, 64, None) == OK
+    assert app(P, P, 2, 5, 8, 128, P, None, P, 64, None) == NULL
+    assert app(P, P + 4, 2, 5, 8, 128, P, P, P, 64, None) == ALIGN
+    assert app(P, P, 2, 5, 8, 100, P, P, P, 64, None) == SHAPE
+    assert app(P, P, 2, 5, 8, 128, P, P, P, 48, None) == SHAPE
+    sm = L.qoq_kv4_smooth_factors
+    assert sm(P, 0, 8, 128, P, None) == SHAPE
+    assert sm(None, 4, 8, 128, P, None) == NULL
+    assert sm(P, 4, 8, 128, P + 2, None) == ALIGN
+
+
 def test_status_strings():
     for s in range(8):
         assert qoq.qoq_status_string(s)

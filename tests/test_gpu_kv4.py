@@ -1,0 +1,210 @@
+"""KV4 decode attention with SmoothAttention scaling against its oracle.
+
+Smoothing factors, cache codes, scales and zeros bit-exact (read through
+the documented layout, after appends that start mid-block and append one
+token at a time); the attention output within the error bound of its fp32
+scores, fp16 probabilities and fp16 dequantized values; exact cases
+(one-token contexts give the dequantized value bit for bit, empty contexts
+give 0); every split of the contexts; the full Llama-3-8B-shaped workload on
+sampled heads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from kv4_layout import decode_cache
+
+qoq = pytest.importorskip("bit_integer_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D = 128
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return torch.from_numpy(a.view(np.uint16)).view(torch.float16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def _factors(k_calib):
+    """Smoothing factors from the same calibration keys on both sides: the
+    library's (device) and the oracle's (host), which must agree bit for bit."""
+    lam_d = qoq.kv4_smooth_factors(_dev(k_calib))
+    lam = oracle.smooth_factors(k_calib)
+    torch.cuda.synchronize()
+    assert np.array_equal(lam_d.cpu().numpy().view(np.uint16), lam.view(np.uint16))
+    return lam, lam_d
+
+
+def _build(B, H, Hkv, lens, C, seed, chunks=None):
+    """Cache filled through qoq_kv4_append (optionally in several calls);
+    returns (q, k, v, lam (oracle), lam_d (library), cache_d)."""
+    q, k, v = wl.make_attention(B, H, Hkv, D, lens, seed=seed)
+    T = k.shape[1]
+    lam, lam_d = _factors(k.reshape(-1, Hkv, D))
+    cache = qoq.kv4_alloc_cache(B, Hkv, C, DEV)
+    cache.fill_(0xAB)                      # never-written tokens hold garbage
+    bounds = chunks or [T]
+    pos = 0
+    for end in bounds:
+        n = end - pos
+        if n > 0:
+            start = _dev(np.full(B, pos, np.int32))
+            qoq.kv4_append(_dev(k[:, pos:end]), _dev(v[:, pos:end]), lam_d, start, cache, C)
+        pos = end
+    torch.cuda.synchronize()
+    return q, k, v, lam, lam_d, cache
+
+
+def _check_cache(cache, k, v, lam, B, Hkv, C, T):
+    got = decode_cache(cache.cpu().numpy(), B, Hkv, C)
+    ref = oracle.kv4_encode(k, v, lam)
+    for n in ("kc", "vc"):
+        assert np.array_equal(got[n][:, :T], ref[n]), n
+    for n in ("ks", "vs"):
+        assert np.array_equal(got[n][:, :T].view(np.uint16), ref[n].view(np.uint16)), n
+    for n in ("kz", "vz"):
+        assert np.array_equal(got[n][:, :T].astype(np.int64), ref[n].astype(np.int64)), n
+    return ref
+
+
+def _tolerance(ref, res, lens):
+    """|o - o_exact| bound per output: fp16 output rounding, fp16 values and
+    probabilities, fp32 accumulation over the context, and score errors
+    (fp32 sums of 128 products and of the query) moving the weights."""
+    qs = res["qs"].astype(np.float64)                     # [B, H, D]
+    B, H, _ = qs.shape
+    Hkv = ref["ks"].shape[2]
+    G = H // Hkv
+    tol = np.zeros((B, H, D))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(H):
+            sk = np.abs(ref["ks"][b, :n, h // G].astype(np.float64)).max()
+            dz = sk * np.abs(qs[b, h]).sum() * 2.0 ** -12 / math.sqrt(D)
+            rel = 2.0 ** -10 + (n + 64) * 2.0 ** -23 + 2.0 * dz
+            tol[b, h] = 2.0 ** -11 * np.abs(res["o"][b, h]) + rel * res["a"][b, h] + 2.0 ** -24
+    return tol
+
+
+def _run(B, H, Hkv, lens, C, seed, monkeypatch, splits=None, chunks=None):
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    if splits:
+        monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
+    print(f"\n[gpu-case] kv4 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits}",
+          flush=True)
+    q, k, v, lam, lam_d, cache = _build(B, H, Hkv, lens, C, seed, chunks)
+    T = k.shape[1]
+    ref = _check_cache(cache, k, v, lam, B, Hkv, C, T)
+    res = oracle.kv4_decode_attention(q, lam, ref, lens, H // Hkv)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(np.asarray(lens, np.int32)),
+                                 int(max(lens)), Hkv)
+    torch.cuda.synchronize()
+    got = o.cpu().float().numpy().astype(np.float64)
+    tol = _tolerance(ref, res, lens)
+    bad = np.abs(got - res["o"]) > tol
+    assert not bad.any(), (f"{bad.sum()} outputs outside the bound, first at {np.argwhere(bad)[:3]}, "
+                           f"err {np.abs(got - res['o'])[bad][:3]}, tol {tol[bad][:3]}")
+    return got, res, ref
+
+
+def test_smooth_factors_exact():
+    rng = np.random.default_rng(3)
+    kc = (rng.standard_normal((300, 4, D)) * np.exp(rng.standard_normal((1, 4, D)))).astype(np.float16)
+    kc[:, 1, 7] = 0
+    kc[:, 2, 9] = np.float16(-3.0)
+    lam = qoq.kv4_smooth_factors(_dev(kc))
+    torch.cuda.synchronize()
+    ref = oracle.smooth_factors(kc)
+    assert np.array_equal(lam.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+    assert float(ref[1, 7]) == 1.0
+
+
+@pytest.mark.parametrize("B,H,Hkv,lens,C", [
+    (3, 8, 2, [1, 33, 100], 128),          # ragged, partial blocks
+    (2, 4, 4, [64, 31], 64),               # no grouping (G = 1)
+    (2, 16, 1, [200, 5], 256),             # 16 query heads on one KV head
+    (4, 32, 8, [90, 0, 17, 128], 128),     # an empty context
+])
+def test_attention_parity(B, H, Hkv, lens, C, monkeypatch):
+    got, res, _ = _run(B, H, Hkv, lens, C, seed=B + H + C, monkeypatch=monkeypatch)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_attention_every_split(splits, monkeypatch):
+    _run(3, 8, 2, [300, 45, 257], 320, seed=17, monkeypatch=monkeypatch, splits=splits)
+
+
+def test_appends_in_pieces(monkeypatch):
+    """Appends that start mid-block, then single tokens (decode steps): the
+    cache equals one append of everything."""
+    _run(2, 8, 2, [70, 70], 96, seed=23, monkeypatch=monkeypatch, chunks=[13, 45, 46, 47, 70])
+
+
+def test_single_token_context_is_exact(monkeypatch):
+    """One cached token: the output is its dequantized value fp16((u - z) s)
+    bit for bit, whatever the query."""
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    B, H, Hkv, C = 3, 8, 2, 32
+    q, k, v, lam, lam_d, cache = _build(B, H, Hkv, [1, 1, 1], C, seed=29)
+    ref = oracle.kv4_encode(k, v, lam)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(np.ones(B, np.int32)), 1, Hkv)
+    torch.cuda.synchronize()
+    vh = oracle.kv4_dequantize(ref["vc"], ref["vs"], ref["vz"]).astype(np.float16)   # [B, 1, Hkv, D]
+    want = np.repeat(vh[:, 0], H // Hkv, axis=1)
+    assert np.array_equal(o.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+def test_zero_query_is_mean(monkeypatch):
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    B, H, Hkv, C = 2, 4, 2, 128
+    lens = [100, 37]
+    q, k, v, lam, lam_d, cache = _build(B, H, Hkv, lens, C, seed=31)
+    q[:] = 0
+    ref = oracle.kv4_encode(k, v, lam)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(np.asarray(lens, np.int32)), 100, Hkv)
+    torch.cuda.synchronize()
+    vh = oracle.kv4_dequantize(ref["vc"], ref["vs"], ref["vz"])
+    got = o.cpu().float().numpy().astype(np.float64)
+    for b, n in enumerate(lens):
+        for h in range(H):
+            mean = vh[b, :n, h // 2].mean(axis=0)
+            a = np.abs(vh[b, :n, h // 2]).mean(axis=0)
+            assert np.all(np.abs(got[b, h] - mean) <= 2.0 ** -11 * np.abs(mean) + 2.0 ** -9 * a + 1e-7)
+
+
+def test_llama_workload_sampled_heads(monkeypatch):
+    """The Llama-3-8B-shaped workload (64 sequences, 512-2048 tokens) at full
+    size, in the launch configuration the benchmark times; the oracle checks
+    a sample of (sequence, head) pairs one by one."""
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    w = wl.ATTN_WORKLOADS["llama3_8b_attn"]
+    q, k, v, lens = wl.make_attention_case(w)
+    C = int(-(-lens.max() // 32) * 32)
+    print(f"\n[gpu-case] kv4 llama workload B={w.B} C={C}", flush=True)
+    lam, lam_d = _factors(k[:4].reshape(-1, w.H_kv, D))
+    cache = qoq.kv4_alloc_cache(w.B, w.H_kv, C, DEV)
+    qoq.kv4_append(_dev(k), _dev(v), lam_d, _dev(np.zeros(w.B, np.int32)), cache, C)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(lens), int(lens.max()), w.H_kv)
+    torch.cuda.synchronize()
+    got = o.cpu().float().numpy().astype(np.float64)
+    G = w.H // w.H_kv
+    rng = np.random.default_rng(5)
+    for b in rng.choice(w.B, 6, replace=False):
+        n = int(lens[b])
+        sub = dict(k=k[b:b + 1, :n], v=v[b:b + 1, :n])
+        enc = oracle.kv4_encode(sub["k"], sub["v"], lam)
+        res = oracle.kv4_decode_attention(q[b:b + 1], lam, enc, [n], G)
+        tol = _tolerance(enc, res, [n])
+        assert np.all(np.abs(got[b:b + 1] - res["o"]) <= tol), b

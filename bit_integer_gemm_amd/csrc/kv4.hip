@@ -22,8 +22,9 @@
 // order of v_mfma_f32_16x16x32_f16, so every lane fetches its operands and
 // their scales with 16-byte loads and no address arithmetic in the loop:
 //   key block (32 tokens): 16 bytes at ((tile * 4 + g) * 16 + t) * 16 hold
-//     token 16 tile + t, dims 32 st + 8 g + e (word st, e = 0..7): byte b of
-//     a word holds dim e = b in the low nibble and e = b + 4 in the high one;
+//     token 16 tile + t, dims 32 st + 8 g + e (word st, e = 0..7); element e
+//     of a word sits at bit 4 (e / 2) + 16 (e % 2), so (w >> 4p) & 0x000F000F
+//     is the pair e = 2p, 2p + 1 in the two 16-bit halves;
 //   value block (32 tokens): 4 bytes at ((g * 16 + d) * 8 + c) * 4 hold dim
 //     16 c + d of tokens pi(8 g + e), e = 0..7, same nibble order, where
 //     pi(8 g + e) = 4 g + e (e < 4), 16 + 4 g + e - 4 (e >= 4);
@@ -125,11 +126,12 @@ __global__ void __launch_bounds__(256) kv4_append_keys_kernel(
     vec_params(v0, v1, sv, zv);
     const float fk = h2f(sk);
     const int c0 = vec_code(k0, fk, zk), c1 = vec_code(k1, fk, zk);
-    // word wi = lane / 4 holds dims 8 wi + e; lane 4wi + r holds e = 2r, 2r + 1;
-    // byte b of the word = code(e = b) | code(e = b + 4) << 4
-    const int up = __shfl_down(c0 | (c1 << 8), 2, 64);     // lanes 4wi+2, 4wi+3 -> 4wi, 4wi+1
-    const uint32_t half16 = uint32_t(c0 | ((up & 0xff) << 4)) | (uint32_t(c1 | (((up >> 8) & 0xff) << 4)) << 8);
-    const uint32_t hi16 = __shfl_down(half16, 1, 64);
+    // word wi = lane / 4 holds dims 8 wi + e; lane 4wi + r holds e = 2r and
+    // 2r + 1, which sit at bits 4r and 16 + 4r of the word
+    const int r4 = 4 * (lane & 3);
+    uint32_t word = (uint32_t(c0) << r4) | (uint32_t(c1) << (16 + r4));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
     uint8_t* region = cache + region_offset(int64_t(b) * Hkv + h, C);
     const int64_t blk = pos / kBlk;
     const int tt = int(pos % kBlk);
@@ -137,7 +139,7 @@ __global__ void __launch_bounds__(256) kv4_append_keys_kernel(
         const int wi = lane >> 2;
         const int st = wi >> 2, g = wi & 3;
         const int64_t off = blk * kBlkBytes + ((tt >> 4) * 4 + g) * 256 + (tt & 15) * 16 + 4 * st;
-        *reinterpret_cast<uint32_t*>(region + off) = (half16 & 0xffffu) | (hi16 << 16);
+        *reinterpret_cast<uint32_t*>(region + off) = word;
     }
     if (lane < 3) {
         // k-index of the token in its block: lane group g = (tt % 16) / 4,
@@ -180,7 +182,7 @@ __global__ void __launch_bounds__(256) kv4_append_values_kernel(
         const int z = int(meta[128 + 8 * g + e] >> 4);
         const float x = h2f(v[((int64_t(b) * Tn + i) * Hkv + h) * kD + 16 * c + d]);
         const uint32_t code = uint32_t(vec_code(x, sc, z));
-        const int sh = 8 * (e & 3) + 4 * (e >> 2);
+        const int sh = 4 * (e >> 1) + 16 * (e & 1);
         wv = (wv & ~(0xfu << sh)) | (code << sh);
         any = true;
     }
@@ -190,15 +192,17 @@ __global__ void __launch_bounds__(256) kv4_append_values_kernel(
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
-// Eight nibbles of a word (byte b: e = b low, e = b + 4 high) -> fp16 pairs
-// of 1024 + code in e order. The byte permute takes the 0x64 exponent bytes
-// from c64 = 0x64646464, so one AND finishes each pair.
-__device__ __forceinline__ void unpack8(uint32_t w, uint32_t c64, h2 (&r)[4]) {
-    const uint32_t w4 = w >> 4;
-    r[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w, 0x04010400u) & 0xff0fff0fu);
-    r[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w, 0x04030402u) & 0xff0fff0fu);
-    r[2] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w4, 0x04010400u) & 0xff0fff0fu);
-    r[3] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, w4, 0x04030402u) & 0xff0fff0fu);
+// Eight codes of a word (element e at bit 4 (e / 2) + 16 (e % 2)) -> four
+// fp16 pairs in e order.
+//   unpack_tiny: the fp16 bit patterns of code * 2^-24 (subnormals, exact);
+//   unpack_1024: 1024 + code (exponent bits 0x64 or-ed in).
+__device__ __forceinline__ void unpack_tiny(uint32_t w, uint32_t m, h2 (&r)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = __builtin_bit_cast(h2, (w >> (4 * p)) & m);
+}
+__device__ __forceinline__ void unpack_1024(uint32_t w, uint32_t m, uint32_t e64, h2 (&r)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = __builtin_bit_cast(h2, ((w >> (4 * p)) & m) | e64);
 }
 
 __device__ __forceinline__ v8h join(const h2 (&r)[4]) {
@@ -301,6 +305,11 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
         r.z = *reinterpret_cast<const uint2*>(mb + 128 + 8 * g);
     };
     const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
+    // one code per 16-bit half; held in a VGPR so that mask-and-or fuses
+    // into one v_and_or_b32 with the exponent constant in an SGPR
+    uint32_t nib;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib));
+    const uint32_t e64 = __builtin_amdgcn_readfirstlane(0x64006400u);
     auto compute = [&](const Blk& r, int blk) {
         const int tbase = blk * kBlk;
         auto valid = [&](int e) {
@@ -311,7 +320,9 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
         // zero bytes z_k | z_v << 4 of the lane's tokens e = 0..3, 4..7
         const uint32_t zk03 = r.z.x & 0x0f0f0f0fu, zk47 = r.z.y & 0x0f0f0f0fu;
         const uint32_t zv03 = (r.z.x >> 4) & 0x0f0f0f0fu, zv47 = (r.z.y >> 4) & 0x0f0f0f0fu;
-        // scores: S[token, query] = q~ . u (u exact small integers)
+        // scores: S[token, query] = q~ . u. The key codes enter the MFMA
+        // as the fp16 subnormals u * 2^-24 (their bit patterns, exact);
+        // products and sums are exact-scaled fp32, undone by the 2^24 below.
         float zs[8];
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -321,9 +332,7 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 h2 u[4];
-                unpack8(kw[st], c64, u);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = u[i] - h2{_Float16(1024.0f), _Float16(1024.0f)};
+                unpack_tiny(kw[st], nib, u);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), qop[st], acc, 0, 0, 0);
             }
 #pragma unroll
@@ -331,7 +340,8 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
                 const int e = 4 * tile + i;
                 const h2 sk2 = __builtin_bit_cast(h2, skw[e >> 1]);
                 const float zk = float(((tile ? zk47 : zk03) >> (8 * i)) & 0xffu);
-                const float sc = (acc[i] - zk * qsum) * (float(sk2[e & 1]) * kScale);
+                const float sc = __builtin_fmaf(acc[i], 16777216.0f, -zk * qsum) *
+                                 (float(sk2[e & 1]) * kScale);
                 zs[e] = valid(e) ? sc : -INFINITY;
             }
         }
@@ -377,7 +387,7 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             h2 u[4];
-            unpack8(vw[c], c64, u);
+            unpack_1024(vw[c], nib, e64, u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) u[i] = (u[i] - zz[i]) * ss[i];
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pop, o[c], 0, 0, 0);
@@ -386,13 +396,15 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
 
     // the wave's blocks: blk0 + wave, + 4, ...; the next block's loads are
     // in flight while one is computed
-    Blk cur, nxt;
+    Blk ra, rb;
     int bi = blk0 + wave;
-    if (bi < blk1) load(cur, bi);
-    for (; bi < blk1; bi += 4) {
-        if (bi + 4 < blk1) load(nxt, bi + 4);
-        compute(cur, bi);
-        cur = nxt;
+    if (bi < blk1) load(ra, bi);
+    for (; bi < blk1; bi += 8) {
+        if (bi + 4 < blk1) load(rb, bi + 4);
+        compute(ra, bi);
+        if (bi + 4 >= blk1) break;
+        if (bi + 8 < blk1) load(ra, bi + 8);
+        compute(rb, bi + 4);
     }
 
     // merge the four waves: lane (j, g) holds query j, dims 16 c + 4 g + i

@@ -12,6 +12,13 @@ def _pi(k):
     return 4 * g + e if e < 4 else 16 + 4 * g + e - 4
 
 
+def _word_codes(w):
+    """uint32 words -> codes [..., 8]: element e at bit 4 (e // 2) + 16 (e % 2)."""
+    w = w.astype(np.uint64)
+    return np.stack([(w >> (4 * (e // 2) + 16 * (e % 2))) & 15 for e in range(8)],
+                    axis=-1).astype(np.uint8)
+
+
 def decode_cache(cache, B, Hkv, C):
     """dict(kc, ks, kz, vc, vs, vz) with codes [B, C, Hkv, D] uint8 and
     scale fp16 / zero uint16 [B, C, Hkv], from the raw cache bytes."""
@@ -20,16 +27,16 @@ def decode_cache(cache, B, Hkv, C):
     out = {n: None for n in ("kc", "ks", "kz", "vc", "vs", "vz")}
     kc = np.zeros((B, C, Hkv, D), np.uint8)
     vc = np.zeros((B, C, Hkv, D), np.uint8)
-    # key block [tile 2][g 4][t 16][word st 4][byte 4]; byte b: e=b low, e=b+4 high
-    kb = a[:, :, :nblk * 2048].reshape(B, Hkv, nblk, 2, 4, 16, 4, 4)
-    lo, hi = kb & 15, kb >> 4
-    codes = np.concatenate([lo, hi], axis=-1)          # [..., st, e 0..7]
+    # key block [tile 2][g 4][t 16][word st 4] (uint32); element e of a word
+    # at bit 4 (e // 2) + 16 (e % 2)
+    kb = a[:, :, :nblk * 2048].copy().view(np.uint32).reshape(B, Hkv, nblk, 2, 4, 16, 4)
+    codes = _word_codes(kb)                              # [..., st, e 0..7]
     # axes: B, Hkv, blk, tile, g, t, st, e -> token 32 blk + 16 tile + t, dim 32 st + 8 g + e
     codes = codes.transpose(0, 1, 2, 3, 5, 6, 4, 7).reshape(B, Hkv, C, D)
     kc[:] = codes.transpose(0, 2, 1, 3)
-    # value block [g 4][d 16][c 8][byte 4]: dim 16 c + d, k-index 8g + e
-    vb = a[:, :, nblk * 2048:nblk * 4096].reshape(B, Hkv, nblk, 4, 16, 8, 4)
-    vcodes = np.concatenate([vb & 15, vb >> 4], axis=-1)   # [B, Hkv, blk, g, d, c, e]
+    # value block [g 4][d 16][c 8] (uint32): dim 16 c + d, k-index 8g + e
+    vb = a[:, :, nblk * 2048:nblk * 4096].copy().view(np.uint32).reshape(B, Hkv, nblk, 4, 16, 8)
+    vcodes = _word_codes(vb)                              # [B, Hkv, blk, g, d, c, e]
     tok = np.array([[_pi(8 * g + e) for e in range(8)] for g in range(4)])
     for g in range(4):
         for e in range(8):

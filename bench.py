@@ -472,7 +472,10 @@ def kv4_attention_bench(torch, qoq, blocker, dev, ws, iters, keys=KV4_WORKLOADS)
         del k, v
         lam = qoq.kv4_smooth_factors(kd[:4].reshape(-1, w.H_kv, w.D))
         cache = qoq.kv4_alloc_cache(w.B, w.H_kv, C, dev)
-        qoq.kv4_append(kd, vd, lam, torch.zeros(w.B, dtype=torch.int32, device=dev), cache, C)
+        zeros = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        qoq.kv4_append(kd, vd, lam, zeros, cache, C)
+        cache16 = qoq.kv16_alloc_cache(w.B, w.H_kv, C, dev)
+        qoq.kv16_append(kd, vd, zeros, cache16, C)
         del kd, vd
         n_copies = int(min(64, max(2, -(-ROTATE_BYTES // cache.numel()))))
         caches = [cache] + [cache.clone() for _ in range(n_copies - 1)]
@@ -496,14 +499,30 @@ def kv4_attention_bench(torch, qoq, blocker, dev, ws, iters, keys=KV4_WORKLOADS)
             if rc:
                 raise RuntimeError(f"kv4 attention: {qoq.qoq_status_string(rc)}")
         t = per_launch_times(torch, blocker, [calls], max(iters, len(calls)))[0]
+        # the same attention on an fp16 cache (what the 4-bit cache is set against)
+        n16 = int(min(64, max(2, -(-ROTATE_BYTES // cache16.numel()))))
+        caches16 = [cache16] + [cache16.clone() for _ in range(n16 - 1)]
+        calls16 = [lambda c=c: L.qoq_kv16_decode_attention(qd.data_ptr(), w.B, w.H, w.H_kv, w.D,
+                                                           c.data_ptr(), C, lens_d.data_ptr(),
+                                                           max_len, o.data_ptr(), wsp, wsb, st())
+                   for c in caches16]
+        for cl in calls16[:2]:
+            rc = cl()
+            if rc:
+                raise RuntimeError(f"kv16 attention: {qoq.qoq_status_string(rc)}")
+        t16 = per_launch_times(torch, blocker, [calls16], max(iters, len(calls16)))[0]
+        del caches16, cache16
         b = wl.attention_bytes(lens, w.H, w.H_kv, w.D)
+        b16 = int(lens.sum()) * w.H_kv * w.D * 4 + 2 * w.B * w.H * w.D * 2
         out.append(dict(workload=key, B=w.B, H=w.H, H_kv=w.H_kv, D=w.D,
                         tokens=int(lens.sum()), max_len=max_len,
                         splits=int(L.qoq_kv4_attention_workspace_bytes(w.B, w.H, w.H_kv, w.D, max_len)
                                    // (w.B * w.H * 132 * 4)) or 1,
                         us=round(t * 1e6, 2), bytes=b, gbs=round(b / t / 1e9, 1),
                         hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                        fp16_kv_bytes=int(lens.sum()) * w.H_kv * w.D * 4))
+                        fp16_kv_us=round(t16 * 1e6, 2), fp16_kv_bytes=b16,
+                        fp16_kv_hbm_frac=round(b16 / t16 / 1e9 / HBM_PEAK_GBS, 4),
+                        kv4_speedup=round(t16 / t, 2)))
         del caches, cache, o
         torch.cuda.empty_cache()
     return out

@@ -35,7 +35,7 @@ __all__ = [
     "w8a8_pack_weights", "w8a8_gemm", "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_gemm",
     "w4a16_pack_weights", "w4a16_gemm",
     "kv4_cache_bytes", "kv4_alloc_cache", "kv4_smooth_factors", "kv4_append",
-    "kv4_decode_attention",
+    "kv4_decode_attention", "kv16_alloc_cache", "kv16_append", "kv16_decode_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -121,6 +121,13 @@ def lib() -> ctypes.CDLL:
         L.qoq_kv4_decode_attention.argtypes = [vp, i64, i64, i64, i64, vp, vp, i64, vp, i64, vp,
                                                vp, sz, vp]
         L.qoq_kv4_decode_attention.restype = ctypes.c_int
+        L.qoq_kv16_cache_bytes.argtypes = [i64, i64, i64, i64]
+        L.qoq_kv16_cache_bytes.restype = sz
+        L.qoq_kv16_append.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, vp]
+        L.qoq_kv16_append.restype = ctypes.c_int
+        L.qoq_kv16_decode_attention.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp, i64, vp, vp,
+                                                sz, vp]
+        L.qoq_kv16_decode_attention.restype = ctypes.c_int
         L.qoq_w4a16_weight_bytes.argtypes = [i64, i64]
         L.qoq_w4a16_weight_bytes.restype = sz
         L.qoq_w4a16_pack_weights.argtypes = [vp, i64, i64, vp, vp]
@@ -530,4 +537,47 @@ def kv4_decode_attention(q: torch.Tensor, lam: torch.Tensor, cache: torch.Tensor
                                           cache.data_ptr(), capacity, lens.data_ptr(), max_len,
                                           out.data_ptr(), ws_ptr, wsb, _stream(dev)),
            "qoq_kv4_decode_attention")
+    return out
+
+
+def kv16_alloc_cache(B: int, H_kv: int, capacity: int, device) -> torch.Tensor:
+    """Device buffer for the fp16 comparison cache."""
+    nbytes = int(lib().qoq_kv16_cache_bytes(B, H_kv, capacity, KV4_HEAD_DIM))
+    if nbytes == 0:
+        raise QoQError(2, "qoq_kv16_cache_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def kv16_append(k: torch.Tensor, v: torch.Tensor, start: torch.Tensor, cache: torch.Tensor,
+                capacity: int) -> None:
+    _need_gpu(k, "k", torch.float16)
+    _need_gpu(v, "v", torch.float16)
+    _need_gpu(start, "start", torch.int32)
+    _need_gpu(cache, "cache", torch.uint8)
+    if k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must both be [B, T_new, H_kv, D]")
+    B, T, H_kv, D = k.shape
+    _check(lib().qoq_kv16_append(k.data_ptr(), v.data_ptr(), B, T, H_kv, D, start.data_ptr(),
+                                 cache.data_ptr(), capacity, _stream(k.device)), "qoq_kv16_append")
+
+
+def kv16_decode_attention(q: torch.Tensor, cache: torch.Tensor, capacity: int, lens: torch.Tensor,
+                          max_len: int, H_kv: int, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[Workspace] = None) -> torch.Tensor:
+    """out [B, H, D] fp16 = softmax(q k^T / sqrt(D)) v over the fp16 cache."""
+    _need_gpu(q, "q", torch.float16)
+    _need_gpu(cache, "cache", torch.uint8)
+    _need_gpu(lens, "lens", torch.int32)
+    B, H, D = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
+    wsb = int(lib().qoq_kv4_attention_workspace_bytes(B, H, H_kv, D, max_len))
+    ws_ptr = None
+    if wsb:
+        ws = (workspace or _default_workspace(dev)).get(wsb)
+        ws_ptr, wsb = ws.data_ptr(), ws.numel()
+    _check(lib().qoq_kv16_decode_attention(q.data_ptr(), B, H, H_kv, D, cache.data_ptr(), capacity,
+                                           lens.data_ptr(), max_len, out.data_ptr(), ws_ptr, wsb,
+                                           _stream(dev)), "qoq_kv16_decode_attention")
     return out

@@ -353,6 +353,52 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
+size_t qoq_kv16_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D) {
+    if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || B == 0) return 0;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return 0;
+    return size_t(qoq::kv16_cache_bytes(B, H_kv, capacity));
+}
+
+qoq_status qoq_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t T_new,
+                           int64_t H_kv, int64_t D, const int32_t* start, void* cache,
+                           int64_t capacity, void* stream) {
+    if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || T_new < 0 || T_new > kKv4MaxCapacity)
+        return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (B == 0 || T_new == 0) return QOQ_OK;
+    if (B * T_new * H_kv > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    if (k == nullptr || v == nullptr || start == nullptr || cache == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(k) || misaligned(v) || misaligned(cache)) return QOQ_ERR_ALIGN;
+    const hipError_t e = qoq::launch_kv16_append(k, v, B, T_new, H_kv, start,
+                                                 static_cast<uint8_t*>(cache), capacity,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+qoq_status qoq_kv16_decode_attention(const uint16_t* q, int64_t B, int64_t H, int64_t H_kv,
+                                     int64_t D, const void* cache, int64_t capacity,
+                                     const int32_t* lens, int64_t max_len, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    const qoq_status st = check_kv4_heads(B, H, H_kv, D);
+    if (st != QOQ_OK) return st;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (max_len < 0 || max_len > capacity) return QOQ_ERR_SHAPE;
+    if (B == 0) return QOQ_OK;
+    if (q == nullptr || cache == nullptr || lens == nullptr || out == nullptr) return QOQ_ERR_NULL;
+    if (misaligned(q) || misaligned(cache) || misaligned(out)) return QOQ_ERR_ALIGN;
+    const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
+    if (p.grid > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    const int64_t need = qoq::kv4_workspace_bytes(p, B, H);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < size_t(need)) return QOQ_ERR_WORKSPACE;
+        if (misaligned(workspace)) return QOQ_ERR_ALIGN;
+    }
+    const hipError_t e = qoq::launch_kv16_attention(
+        p, q, B, H, H_kv, static_cast<const uint8_t*>(cache), capacity, lens, max_len, out,
+        static_cast<float*>(need > 0 ? workspace : nullptr), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
 const char* qoq_status_string(int status) {
     switch (status) {
         case QOQ_OK: return "ok";

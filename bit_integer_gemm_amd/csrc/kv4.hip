@@ -189,6 +189,40 @@ __global__ void __launch_bounds__(256) kv4_append_values_kernel(
     if (any) *wp = wv;
 }
 
+// fp16 cache append (the comparison point): one wave per (sequence, new
+// token, KV head), lane l stores dims 2l, 2l + 1 of the key and the value
+// at their places in the fp16 MFMA-ordered layout.
+__global__ void __launch_bounds__(256) kv16_append_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B, int Tn, int Hkv,
+    const int32_t* __restrict__ start, uint8_t* __restrict__ cache, int64_t C) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (w >= int64_t(B) * Tn * Hkv) return;
+    const int h = int(w % Hkv);
+    const int i = int((w / Hkv) % Tn);
+    const int b = int(w / (int64_t(Hkv) * Tn));
+    const int64_t pos = int64_t(max(start[b], 0)) + i;
+    if (pos >= C) return;
+    const int64_t src = ((int64_t(b) * Tn + i) * Hkv + h) * kD + 2 * lane;
+    const uint32_t kk = *reinterpret_cast<const uint32_t*>(k + src);
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + src);
+    uint8_t* rg = cache + (int64_t(b) * Hkv + h) * C * (4 * kD);
+    const int64_t blk = pos / kBlk;
+    const int tt = int(pos % kBlk);
+    const int d = 2 * lane;
+    const int st = d >> 5, g = (d & 31) >> 3, e = d & 7;
+    *reinterpret_cast<uint32_t*>(rg + blk * 4 * kBlkBytes + (((tt >> 4) * 4 + g) * 16 + (tt & 15)) * 64 +
+                                 16 * st + 2 * e) = kk;
+    const int gt = (tt & 15) >> 2, et = (tt & 3) + 4 * (tt >> 4);
+    uint8_t* vb = rg + (C / kBlk) * 4 * kBlkBytes + blk * 4 * kBlkBytes;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int dd = d + r;
+        *reinterpret_cast<uint16_t*>(vb + ((gt * 16 + (dd & 15)) * 8 + (dd >> 4)) * 16 + 2 * et) =
+            uint16_t(vv >> (16 * r));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
@@ -230,6 +264,12 @@ struct AttnArgs {
 // split's blocks w, w + 4, ...; per block: 2 score MFMAs tiles x 4 steps
 // (tokens x queries), online softmax per query, 8 value MFMAs (dims x
 // queries). The four waves' states are merged in LDS at the end.
+// kF16: the same kernel on an fp16 cache (the comparison point for what the
+// 4-bit cache buys): keys and values are the MFMA operands as stored, the
+// query is used unsmoothed, nothing is dequantized. Per 32-token block the
+// fp16 layout holds keys [tile 2][g 4][t 16][st 4][8 halves] and values
+// [g 4][d 16][c 8][8 halves] (tokens pi(8 g + e)), 8 KiB each.
+template <bool kF16>
 __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,9 +287,10 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     // a split past the end of its context writes nothing: the merge of the
     // splits reads only those that hold tokens
     if (a.splits > 1 && blk0 >= nb) return;
-    const uint8_t* rg = a.cache + region_offset(region, C);
+    const uint8_t* rg = kF16 ? a.cache + int64_t(region) * C * (4 * kD)
+                             : a.cache + region_offset(region, C);
     const uint8_t* kbase = rg;
-    const uint8_t* vbase = rg + (C / kBlk) * kBlkBytes;
+    const uint8_t* vbase = rg + (C / kBlk) * (kF16 ? 4 * kBlkBytes : kBlkBytes);
     const uint8_t* mbase = rg + (C / kBlk) * 2 * kBlkBytes;
     const bool qvalid = j < a.G;
     const int qh = h * a.G + min(j, a.G - 1);
@@ -261,7 +302,8 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     for (int st = 0; st < 4; ++st) {
         const int d0 = 32 * st + 8 * g;
         const uint4 qq = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + qh) * kD + d0);
-        const uint4 ll = *reinterpret_cast<const uint4*>(a.lam + h * kD + d0);
+        const uint4 ll = kF16 ? uint4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}
+                              : *reinterpret_cast<const uint4*>(a.lam + h * kD + d0);
         const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w}, lw[4] = {ll.x, ll.y, ll.z, ll.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -287,12 +329,29 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     auto kofs = [&](int tile) { return (tile * 4 + g) * 256 + j * 16; };
     const int vofs = (g * 16 + j) * 32;
     // per block: key codes (2 tiles), value codes, and the lane's 8 entries
-    // of each metadata array (s_k, s_v, zero bytes)
-    struct Blk {
+    // of each metadata array (s_k, s_v, zero bytes); or the fp16 operands
+    struct Blk4 {
         uint4 k0, k1, v0, v1, sk, sv;
         uint2 z;
     };
-    auto load = [&](Blk& r, int blk) {
+    struct Blk16 {
+        uint4 k[8], v[8];
+    };
+    using Blk = typename std::conditional<kF16, Blk16, Blk4>::type;
+    auto load = [&](auto& r, int blk) {
+      if constexpr (kF16) {
+        const uint8_t* kb = kbase + int64_t(blk) * 4 * kBlkBytes;
+        const uint8_t* vb = vbase + int64_t(blk) * 4 * kBlkBytes;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                r.k[4 * tile + st] = *reinterpret_cast<const uint4*>(
+                    kb + ((tile * 4 + g) * 16 + j) * 64 + 16 * st);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            r.v[c] = *reinterpret_cast<const uint4*>(vb + (g * 16 + j) * 128 + 16 * c);
+      } else {
         const uint8_t* kb = kbase + int64_t(blk) * kBlkBytes;
         const uint8_t* vb = vbase + int64_t(blk) * kBlkBytes;
         const uint8_t* mb = mbase + int64_t(blk) * kMetaBlkBytes;
@@ -303,6 +362,7 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
         r.sk = *reinterpret_cast<const uint4*>(mb + 16 * g);
         r.sv = *reinterpret_cast<const uint4*>(mb + 64 + 16 * g);
         r.z = *reinterpret_cast<const uint2*>(mb + 128 + 8 * g);
+      }
     };
     const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
     // one code per 16-bit half; held in a VGPR so that mask-and-or fuses
@@ -310,7 +370,63 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     uint32_t nib;
     asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib));
     const uint32_t e64 = __builtin_amdgcn_readfirstlane(0x64006400u);
-    auto compute = [&](const Blk& r, int blk) {
+    // online softmax for query j over a block's 32 tokens; the accumulators
+    // are rescaled only when the running maximum grows by more than 2^8
+    // (probabilities stay below 256 in between). Returns the fp16 P operand.
+    auto softmax = [&](const float (&zs)[8]) {
+        float bm = zs[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zs[e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const bool grow = bm > m + 8.0f;
+        if (__ballot(grow) != 0) {
+            const float fac = grow ? __builtin_amdgcn_exp2f(m - bm) : 1.0f;
+            l *= fac;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c] = o[c] * fac;
+            m = grow ? bm : m;
+        }
+        v8h pop;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(zs[e] - m);
+            l += pe;
+            pop[e] = static_cast<_Float16>(pe);
+        }
+        return pop;
+    };
+    auto compute16 = [&](const Blk16& r, int blk) {
+        const int tbase = blk * kBlk;
+        auto valid = [&](int e) {
+            const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+            return tbase + tok < len;
+        };
+        float zs[8];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, r.k[4 * tile + st]),
+                                                             qop[st], acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zs[4 * tile + i] = valid(4 * tile + i) ? acc[i] * kScale : -INFINITY;
+        }
+        const v8h pop = softmax(zs);
+        // tokens past the context: their values are zeroed (any bits may be there)
+        uint32_t keep[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr)
+            keep[pr] = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 w = r.v[c];
+            const uint4 vm = uint4{w.x & keep[0], w.y & keep[1], w.z & keep[2], w.w & keep[3]};
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, vm), pop, o[c], 0, 0, 0);
+        }
+    };
+    auto compute4 = [&](const Blk4& r, int blk) {
         const int tbase = blk * kBlk;
         auto valid = [&](int e) {
             const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
@@ -345,29 +461,7 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
                 zs[e] = valid(e) ? sc : -INFINITY;
             }
         }
-        // online softmax for query j over the block's 32 tokens; the
-        // accumulators are rescaled only when the running maximum grows by
-        // more than 2^8 (probabilities stay below 256 in between)
-        float bm = zs[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zs[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const bool grow = bm > m + 8.0f;
-        if (__ballot(grow) != 0) {
-            const float fac = grow ? __builtin_amdgcn_exp2f(m - bm) : 1.0f;
-            l *= fac;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) o[c] = o[c] * fac;
-            m = grow ? bm : m;
-        }
-        v8h pop;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(zs[e] - m);
-            l += pe;
-            pop[e] = static_cast<_Float16>(pe);
-        }
+        const v8h pop = softmax(zs);
         // values: (1024 + u) - (1024 + z) = u - z exactly, times s (one
         // rounding); tokens past the context get scale 0 and a neutral zero
         h2 zz[4], ss[4];
@@ -392,6 +486,10 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
             for (int i = 0; i < 4; ++i) u[i] = (u[i] - zz[i]) * ss[i];
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pop, o[c], 0, 0, 0);
         }
+    };
+    auto compute = [&](const Blk& r, int blk) {
+        if constexpr (kF16) compute16(r, blk);
+        else compute4(r, blk);
     };
 
     // the wave's blocks: blk0 + wave, + 4, ...; the next block's loads are
@@ -576,7 +674,32 @@ hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, 
                                 hipStream_t stream) {
     AttnArgs a{q, lam, cache, lens, out, part, C, int(B), int(H), int(Hkv), int(H / Hkv), p.splits,
                p.bps, int(max_len)};
-    hipError_t e = launch_kernel(kv4_attention_kernel, dim3(unsigned(p.grid)), dim3(256), 0, stream, a);
+    hipError_t e = launch_kernel(kv4_attention_kernel<false>, dim3(unsigned(p.grid)), dim3(256), 0,
+                                 stream, a);
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int rows = int(B * H);
+    return launch_kernel(kv4_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,
+                         (const float*)part, rows, int(H), p.splits, p.bps, lens, int(max_len), C,
+                         out);
+}
+
+int64_t kv16_cache_bytes(int64_t B, int64_t Hkv, int64_t C) { return B * Hkv * C * 4 * kD; }
+
+hipError_t launch_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t Tn,
+                              int64_t Hkv, const int32_t* start, uint8_t* cache, int64_t C,
+                              hipStream_t stream) {
+    const int64_t waves = B * Tn * Hkv;
+    return launch_kernel(kv16_append_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, stream,
+                         k, v, int(B), int(Tn), int(Hkv), start, cache, C);
+}
+
+hipError_t launch_kv16_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,
+                                 int64_t Hkv, const uint8_t* cache, int64_t C, const int32_t* lens,
+                                 int64_t max_len, uint16_t* out, float* part, hipStream_t stream) {
+    AttnArgs a{q, nullptr, cache, lens, out, part, C, int(B), int(H), int(Hkv), int(H / Hkv),
+               p.splits, p.bps, int(max_len)};
+    hipError_t e = launch_kernel(kv4_attention_kernel<true>, dim3(unsigned(p.grid)), dim3(256), 0,
+                                 stream, a);
     if (e != hipSuccess || p.splits == 1) return e;
     const int rows = int(B * H);
     return launch_kernel(kv4_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,

@@ -196,6 +196,14 @@ hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, 
                                 const int32_t* lens, int64_t max_len, uint16_t* out, float* part,
                                 hipStream_t stream);
 
+int64_t kv16_cache_bytes(int64_t B, int64_t Hkv, int64_t C);
+hipError_t launch_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t Tn,
+                              int64_t Hkv, const int32_t* start, uint8_t* cache, int64_t C,
+                              hipStream_t stream);
+hipError_t launch_kv16_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,
+                                 int64_t Hkv, const uint8_t* cache, int64_t C, const int32_t* lens,
+                                 int64_t max_len, uint16_t* out, float* part, hipStream_t stream);
+
 hipError_t launch_linear_fused(const LinearPlan& plan, const uint16_t* x, int64_t M, int64_t K,
                                const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
                                int32_t* acc_debug, hipStream_t stream);

@@ -85,6 +85,21 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
                                     uint16_t* out, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* The comparison point: the same decode attention on an fp16 cache (what the
+ * pages set the 4-bit cache against), 512 bytes per token and KV head
+ * (keys and values as stored, in the same MFMA lane order), queries
+ * unsmoothed: out = softmax(q . k / sqrt(D)) v. Same shapes, errors,
+ * workspace (qoq_kv4_attention_workspace_bytes) and QOQ_KV4_SPLITS as the
+ * KV4 calls. */
+size_t qoq_kv16_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D);
+qoq_status qoq_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t T_new,
+                           int64_t H_kv, int64_t D, const int32_t* start, void* cache,
+                           int64_t capacity, void* stream);
+qoq_status qoq_kv16_decode_attention(const uint16_t* q, int64_t B, int64_t H, int64_t H_kv,
+                                     int64_t D, const void* cache, int64_t capacity,
+                                     const int32_t* lens, int64_t max_len, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,4 +9,5 @@ from .variants import (W8_MAX, INT4_MAX, w8a8_quantize_weights, w8a8_linear,  # 
                        w4a4_linear, w4a16_quantize_weights, w4a16_dequantize,
                        w4a16_linear)
 from .kv4 import (smooth_factors, kv4_quantize, kv4_dequantize,  # noqa: F401
-                  kv4_encode, smooth_query, attention_core, kv4_decode_attention)
+                  kv4_encode, smooth_query, attention_core, kv4_decode_attention,
+                  fp16_decode_attention)

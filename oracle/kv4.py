@@ -128,3 +128,13 @@ def kv4_decode_attention(q, lam, enc, lens, group):
     vh = kv4_dequantize(enc["vc"], enc["vs"], enc["vz"])
     o, a, r = attention_core(qs.astype(np.float64), kh, vh, lens, group)
     return dict(o=o, a=a, r=r, qs=qs)
+
+
+def fp16_decode_attention(q, k, v, lens, group):
+    """The comparison point: the same attention on an fp16 cache, queries
+    unsmoothed (smoothing changes nothing without quantization). Returns
+    dict(o, a, r)."""
+    o, a, r = attention_core(np.asarray(q, dtype=np.float16).astype(np.float64),
+                             np.asarray(k, dtype=np.float16).astype(np.float64),
+                             np.asarray(v, dtype=np.float16).astype(np.float64), lens, group)
+    return dict(o=o, a=a, r=r)

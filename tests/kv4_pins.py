@@ -199,7 +199,22 @@ def pin_brute_force_end_to_end(mod):
             assert abs(acc / sum(w) - res["o"][0, h, d]) <= 1e-12, (h, d)
 
 
+def pin_fp16_path_is_plain_attention(mod):
+    """The fp16 comparison path: one token gives its value; a zero query the
+    mean of the first len values."""
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((2, 5, 1, D)).astype(np.float16)
+    v = rng.standard_normal((2, 5, 1, D)).astype(np.float16)
+    q = rng.standard_normal((2, 2, D)).astype(np.float16)
+    res = mod.fp16_decode_attention(q, k, v, [1, 5], 2)
+    assert np.array_equal(res["o"][0, 0], v[0, 0, 0].astype(np.float64))
+    q0 = np.zeros_like(q)
+    res = mod.fp16_decode_attention(q0, k, v, [1, 5], 2)
+    assert np.allclose(res["o"][1, 1], v[1, :, 0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-12)
+
+
 KV4_PINS = [pin_smooth_factors_hand, pin_kv4_quantize_hand, pin_keys_divided_values_not,
             pin_query_multiplied_per_kv_head, pin_single_token_is_its_value,
             pin_zero_query_is_mean, pin_two_tokens_closed_form, pin_grouped_query_mapping,
-            pin_length_mask, pin_smoothing_identity, pin_bound_terms, pin_brute_force_end_to_end]
+            pin_length_mask, pin_smoothing_identity, pin_bound_terms, pin_brute_force_end_to_end,
+            pin_fp16_path_is_plain_attention]

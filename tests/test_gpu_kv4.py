@@ -208,3 +208,51 @@ def test_llama_workload_sampled_heads(monkeypatch):
         res = oracle.kv4_decode_attention(q[b:b + 1], lam, enc, [n], G)
         tol = _tolerance(enc, res, [n])
         assert np.all(np.abs(got[b:b + 1] - res["o"]) <= tol), b
+
+
+# ---------------------------------------------------------------------------
+# the fp16 comparison path
+# ---------------------------------------------------------------------------
+def _run16(B, H, Hkv, lens, C, seed, monkeypatch, splits=None):
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    if splits:
+        monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
+    print(f"\n[gpu-case] kv16 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits}",
+          flush=True)
+    q, k, v = wl.make_attention(B, H, Hkv, D, lens, seed=seed)
+    cache = qoq.kv16_alloc_cache(B, Hkv, C, DEV)
+    cache.fill_(0xFF)                      # never-written tokens hold NaN bit patterns
+    qoq.kv16_append(_dev(k), _dev(v), _dev(np.zeros(B, np.int32)), cache, C)
+    o = qoq.kv16_decode_attention(_dev(q), cache, C, _dev(np.asarray(lens, np.int32)),
+                                  int(max(lens)), Hkv)
+    torch.cuda.synchronize()
+    res = oracle.fp16_decode_attention(q, k, v, lens, H // Hkv)
+    got = o.cpu().float().numpy().astype(np.float64)
+    tol = np.zeros_like(got)
+    for b, n in enumerate(lens):
+        for h in range(H):
+            rel = 2.0 ** -10 + (n + 64) * 2.0 ** -23 + 2.0 * (D + 8) * 2.0 ** -24 * res["r"][b, h]
+            tol[b, h] = 2.0 ** -11 * np.abs(res["o"][b, h]) + rel * res["a"][b, h] + 2.0 ** -24
+    bad = np.abs(got - res["o"]) > tol
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound, first at {np.argwhere(bad)[:3]}"
+    return got, v
+
+
+@pytest.mark.parametrize("B,H,Hkv,lens,C", [(3, 8, 2, [1, 33, 100], 128), (2, 4, 4, [64, 31], 64),
+                                            (4, 32, 8, [90, 0, 17, 128], 128)])
+def test_fp16_attention_parity(B, H, Hkv, lens, C, monkeypatch):
+    got, _ = _run16(B, H, Hkv, lens, C, seed=41 + B, monkeypatch=monkeypatch)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_fp16_attention_splits(splits, monkeypatch):
+    _run16(3, 8, 2, [300, 45, 257], 320, seed=43, monkeypatch=monkeypatch, splits=splits)
+
+
+def test_fp16_single_token_is_exact(monkeypatch):
+    got, v = _run16(2, 8, 2, [1, 1], 32, seed=47, monkeypatch=monkeypatch)
+    want = np.repeat(v[:, 0].astype(np.float64), 4, axis=1)
+    assert np.array_equal(got, want)

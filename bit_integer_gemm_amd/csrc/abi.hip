@@ -279,11 +279,18 @@ qoq_status check_kv4_heads(int64_t B, int64_t H, int64_t Hkv, int64_t D) {
         return QOQ_ERR_SHAPE;
     return QOQ_OK;
 }
+
+// caches of B x H_kv regions of C tokens (512 bytes per token at most) must
+// have byte offsets far inside int64
+bool kv_cache_fits(int64_t B, int64_t Hkv, int64_t C) {
+    return double(B) * double(Hkv) * double(C) * 512.0 < 4.0e18;
+}
 }  // namespace
 
 size_t qoq_kv4_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D) {
     if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || B == 0) return 0;
     if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return 0;
+    if (!kv_cache_fits(B, H_kv, capacity)) return 0;
     return size_t(qoq::kv4_cache_bytes(B, H_kv, capacity));
 }
 
@@ -302,7 +309,9 @@ qoq_status qoq_kv4_append(const uint16_t* k, const uint16_t* v, int64_t B, int64
                           void* cache, int64_t capacity, void* stream) {
     if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || T_new < 0 || T_new > kKv4MaxCapacity)
         return QOQ_ERR_SHAPE;
-    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity ||
+        !kv_cache_fits(B, H_kv, capacity))
+        return QOQ_ERR_SHAPE;
     if (B == 0 || T_new == 0) return QOQ_OK;
     if (B * T_new * H_kv > (int64_t(1) << 31) ||
         B * H_kv * ((T_new + 31) / 32 + 1) * 512 > (int64_t(1) << 31))
@@ -333,7 +342,9 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
                                     void* stream) {
     const qoq_status st = check_kv4_heads(B, H, H_kv, D);
     if (st != QOQ_OK) return st;
-    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity ||
+        !kv_cache_fits(B, H_kv, capacity))
+        return QOQ_ERR_SHAPE;
     if (max_len < 0 || max_len > capacity) return QOQ_ERR_SHAPE;
     if (B == 0) return QOQ_OK;
     if (q == nullptr || lambda == nullptr || cache == nullptr || lens == nullptr || out == nullptr)
@@ -356,6 +367,7 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
 size_t qoq_kv16_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D) {
     if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || B == 0) return 0;
     if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return 0;
+    if (!kv_cache_fits(B, H_kv, capacity)) return 0;
     return size_t(qoq::kv16_cache_bytes(B, H_kv, capacity));
 }
 
@@ -364,7 +376,9 @@ qoq_status qoq_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int6
                            int64_t capacity, void* stream) {
     if (check_kv4_heads(B, H_kv, H_kv, D) != QOQ_OK || T_new < 0 || T_new > kKv4MaxCapacity)
         return QOQ_ERR_SHAPE;
-    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity ||
+        !kv_cache_fits(B, H_kv, capacity))
+        return QOQ_ERR_SHAPE;
     if (B == 0 || T_new == 0) return QOQ_OK;
     if (B * T_new * H_kv > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
     if (k == nullptr || v == nullptr || start == nullptr || cache == nullptr) return QOQ_ERR_NULL;
@@ -381,7 +395,9 @@ qoq_status qoq_kv16_decode_attention(const uint16_t* q, int64_t B, int64_t H, in
                                      void* workspace, size_t workspace_bytes, void* stream) {
     const qoq_status st = check_kv4_heads(B, H, H_kv, D);
     if (st != QOQ_OK) return st;
-    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity) return QOQ_ERR_SHAPE;
+    if (capacity <= 0 || capacity % 32 != 0 || capacity > kKv4MaxCapacity ||
+        !kv_cache_fits(B, H_kv, capacity))
+        return QOQ_ERR_SHAPE;
     if (max_len < 0 || max_len > capacity) return QOQ_ERR_SHAPE;
     if (B == 0) return QOQ_OK;
     if (q == nullptr || cache == nullptr || lens == nullptr || out == nullptr) return QOQ_ERR_NULL;

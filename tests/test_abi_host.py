@@ -79,6 +79,8 @@ def test_kv4_sizes_and_validation(monkeypatch):
     assert L.qoq_kv4_cache_bytes(2, 8, 100, 128) == 0          # capacity not a multiple of 32
     assert L.qoq_kv4_cache_bytes(2, 8, 64, 64) == 0            # head dim other than 128
     assert L.qoq_kv4_cache_bytes(0, 8, 64, 128) == 0
+    assert L.qoq_kv4_cache_bytes(1 << 30, 4096, 1 << 24, 128) == 0     # offsets beyond int64
+    assert L.qoq_kv16_cache_bytes(64, 8, 2048, 128) == 64 * 8 * 2048 * 512
     # one workgroup per (sequence, KV head) when there are 512 of them: no
     # workspace; few long contexts are split (here 16 ways) and their partial
     # results (132 floats per query head and split) meet in the workspace

@@ -301,7 +301,7 @@ def quantize_act(x: torch.Tensor, out=None):
 
 
 class Workspace:
-    """A zero-filled device buffer, grown on demand, for the workspace
+    """A device buffer, grown on demand, for the workspace
     arguments of qoq_w4a8_gemm and qoq_w4a8_linear. One buffer serves any
     number of sequential calls on one stream."""
 

@@ -20,6 +20,7 @@
 
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -246,12 +247,19 @@ __global__ void __launch_bounds__(64 * KW) gemm_decode_kernel(
 // workgroup -- each wave fetches a share of the fragments into a register
 // ring P groups ahead and writes them to one of two LDS slots -- and all
 // waves read them from there. One barrier per group.
+//
+// Split K: when `part` is given, workgroup z covers only the groups
+// [z * gps, (z + 1) * gps) (gps a multiple of 8, so the record chunks stay
+// aligned) and stores its exact INT32 sums to part[z][m][n] instead of the
+// epilogue; splitk_epilogue_kernel adds the splits (integer addition, so the
+// result equals the unsplit sum bit for bit) and applies the epilogue. This
+// fills the chip for shapes with few column blocks and a long K.
 template <int MT, int CB, int NW, int P>
 __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
     const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_debug) {
+    int32_t* __restrict__ acc_debug, int gps, int32_t* __restrict__ part) {
     constexpr int AF = 2 * MT;                    // A fragments per group
     constexpr int AFW = (AF + NW - 1) / NW;       // fragments fetched per wave
     static_assert(P >= 2 && P % 2 == 0, "ring depth must be even");
@@ -264,6 +272,10 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
     const int nbt = N >> 4;
     const int nb0 = (blockIdx.x * NW + wave) * CB;
     const int m0 = blockIdx.y * 16 * MT;
+    // this workgroup's group range [g0, g0 + cnt); cnt >= 1 by the grid
+    const int g0 = blockIdx.z * gps;
+    const int cnt = min(ng - g0, gps);
+    const int glast = g0 + cnt - 1;
 
     const uint8_t* bptr[CB];
     const uint8_t* rptr[CB];
@@ -297,7 +309,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
     // channel; the loop is unrolled by 8 so the group's slot is static
     uint4 rc_cur[CB], rc_next[CB];
     auto load_rec = [&](uint4 (&dst)[CB], int chunk) {
-        chunk = min(chunk, (ng - 1) >> 3);
+        chunk = min(chunk, glast >> 3);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             dst[cb] = *reinterpret_cast<const uint4*>(rptr[cb] + chunk * (kBlockCols * kRecChunk * 2));
@@ -334,54 +346,56 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
             }
         }
     };
-    // One group step. Every global load is unconditional -- groups past the
-    // last one are clamped to it (cache hits, never used) -- and only LDS
-    // staging and compute are guarded, so the compiler's waits cover exactly
-    // one stage of each ring and never drain them.
+    // One group step (i counts from the range start; groups are g0 + i).
+    // Every global load is unconditional -- groups past the range's last one
+    // are clamped to it (cache hits, never used) -- and only LDS staging and
+    // compute are guarded, so the compiler's waits cover exactly one stage
+    // of each ring and never drain them.
     auto step = [&](int i, int u, bool full) {
         const int p = u % P;
         const int pn = (p + 1) % P;
-        if (i + 1 < ng) stage_a((p + 1) & 1, pn);
-        load_a(pn, min(i + 1 + P, ng - 1));
-        if (full || i < ng) compute(p & 1, p, u);
-        load_b(p, min(i + P, ng - 1));
+        if (i + 1 < cnt) stage_a((p + 1) & 1, pn);
+        load_a(pn, g0 + min(i + 1 + P, cnt - 1));
+        if (full || i < cnt) compute(p & 1, p, u);
+        load_b(p, g0 + min(i + P, cnt - 1));
         if (u == 7) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) rc_cur[cb] = rc_next[cb];
-            load_rec(rc_next, ((i + 1) >> 3) + 1);
+            load_rec(rc_next, ((g0 + i + 1) >> 3) + 1);
         }
         __syncthreads();
     };
 
-    // Prologue: stage group 0, then issue the loads in the same order the
-    // steady state issues them (as if steps -P..-1 had run), so the loop is
-    // entered with the rings in their steady-state shape.
-    load_rec(rc_cur, 0);
-    load_rec(rc_next, 1);
-    load_a(0, 0);
+    // Prologue: stage the range's first group, then issue the loads in the
+    // same order the steady state issues them (as if steps -P..-1 had run),
+    // so the loop is entered with the rings in their steady-state shape.
+    load_rec(rc_cur, g0 >> 3);
+    load_rec(rc_next, (g0 >> 3) + 1);
+    load_a(0, g0);
     stage_a(0, 0);
 #pragma unroll
     for (int j = -P; j < 0; ++j) {
-        load_a((j + 1 + P) % P, min(j + 1 + P, ng - 1));
-        load_b((j + P) % P, min(j + P, ng - 1));
+        load_a((j + 1 + P) % P, g0 + min(j + 1 + P, cnt - 1));
+        load_b((j + P) % P, g0 + min(j + P, cnt - 1));
     }
     __syncthreads();
     static_assert(8 % P == 0, "ring depth must divide the record chunk");
     int i0 = 0;
-    for (; i0 + 8 <= ng; i0 += 8) {
+    for (; i0 + 8 <= cnt; i0 += 8) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) step(i0 + u, u, true);
     }
-    if (i0 < ng) {
+    if (i0 < cnt) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) step(i0 + u, u, false);
     }
 
+    int32_t* pz = part ? part + int64_t(blockIdx.z) * M * N : nullptr;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         if (nb0 + cb >= nbt) continue;
         const int n = 16 * (nb0 + cb) + c;
-        const float sw = h2f(s1[n]);
+        const float sw = pz ? 0.f : h2f(s1[n]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -389,10 +403,48 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
                 const int m = m0 + 16 * mt + 4 * h + r;
                 if (m >= M) continue;
                 const int32_t v = acc[mt][cb][r];
+                if (pz) {
+                    pz[int64_t(m) * N + n] = v;
+                    continue;
+                }
                 if (acc_debug) acc_debug[int64_t(m) * N + n] = v;
                 y[int64_t(m) * N + n] = epilogue_value(v, s_x[m], sw);
             }
     }
+}
+
+// Second pass of a split-K GEMM: thread t sums the S INT32 partials of
+// outputs 4t .. 4t + 3 (one row, N % 16 == 0) in split order and applies the
+// epilogue.
+__global__ void __launch_bounds__(256) splitk_epilogue_kernel(
+    const int32_t* __restrict__ part, int S, int M, int N, const float* __restrict__ s_x,
+    const uint16_t* __restrict__ s1, uint16_t* __restrict__ y, int32_t* __restrict__ acc_debug) {
+    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t MN = int64_t(M) * N;
+    if (4 * t >= MN) return;
+    const int m = int(4 * t / N);
+    const int n = int(4 * t - int64_t(m) * N);
+    int4 sum = *reinterpret_cast<const int4*>(part + 4 * t);
+    for (int z = 1; z < S; ++z) {
+        const int4 v = *reinterpret_cast<const int4*>(part + z * MN + 4 * t);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    if (acc_debug) {   // the debug buffer carries no alignment promise
+        acc_debug[4 * t] = sum.x;
+        acc_debug[4 * t + 1] = sum.y;
+        acc_debug[4 * t + 2] = sum.z;
+        acc_debug[4 * t + 3] = sum.w;
+    }
+    const float sx = s_x[m];
+    uint2 out;
+    out.x = uint32_t(epilogue_value(sum.x, sx, h2f(s1[n]))) |
+            (uint32_t(epilogue_value(sum.y, sx, h2f(s1[n + 1]))) << 16);
+    out.y = uint32_t(epilogue_value(sum.z, sx, h2f(s1[n + 2]))) |
+            (uint32_t(epilogue_value(sum.w, sx, h2f(s1[n + 3]))) << 16);
+    *reinterpret_cast<uint2*>(y + 4 * t) = out;   // y is 16-byte aligned
 }
 
 // 32x32 tile family (large M), built on v_mfma_i32_32x32x32_i8 (the
@@ -417,12 +469,15 @@ __global__ void __launch_bounds__(64 * NW) gemm_lds_kernel(
 //     rings) so two workgroups share a CU: one's barrier waits, LDS latency
 //     and dequantization bursts are covered by the other's MFMAs.
 //   * Epilogue through LDS with 16-byte row-segment stores.
+//   * Split K (as in the shared-activation family): with `part` given,
+//     workgroup row y of the grid covers groups [y * gps, (y + 1) * gps) and
+//     stores its INT32 sums to part[y][m][n] for splitk_epilogue_kernel.
 template <int MT, int CB, int PB, int MINB, int NW>
 __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
     const uint16_t* __restrict__ s1, int N, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_debug) {
+    int32_t* __restrict__ acc_debug, int gps, int32_t* __restrict__ part) {
     constexpr int AF = 4 * MT;                    // A fragments per group
     constexpr int AFW = (AF + NW - 1) / NW;       // fetched per wave
     static_assert(AF * 2 <= 64, "LDS slots above 64 KiB");
@@ -447,6 +502,10 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM;
     const int nbw = tn * BNB + wave * 2 * CB;     // this wave's first 16-column block
+    // this workgroup's group range [g0, g0 + cnt); cnt >= 1 by the grid
+    const int g0 = blockIdx.y * gps;
+    const int cnt = min(ng - g0, gps);
+    const int glast = g0 + cnt - 1;
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)x8, (short)0, int(act_bytes(M, K)), 0x00020000);
@@ -489,15 +548,17 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     // channel; the loop is unrolled by 8 so the group's slot is static
     uint4 rc_cur[CB], rc_next[CB];
     auto load_rec = [&](uint4 (&dst)[CB], int chunk) {
-        chunk = min(chunk, (ng - 1) >> 3);
+        chunk = min(chunk, glast >> 3);
 #pragma unroll
         for (int t = 0; t < CB; ++t)
             dst[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rr, r_lane[t], chunk * (kBlockCols * kRecChunk * 2), 0));
     };
 
-    auto load_a = [&](int g) {
-        g = min(g, ng - 1);
+    // i counts groups from the range start; past its end the last group is
+    // loaded again (cache hits, never used)
+    auto load_a = [&](int i) {
+        const int g = g0 + min(i, cnt - 1);
 #pragma unroll
         for (int u = 0; u < AFW; ++u) {
             const int soff = g * kActGroupBytes + a_soff[u];
@@ -509,8 +570,8 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
         for (int u = 0; u < AFW; ++u)
             if (owns(u)) As[slot][wave + NW * u][lane] = ar[u];
     };
-    auto load_b = [&](int p, int g) {
-        g = min(g, ng - 1);
+    auto load_b = [&](int p, int i) {
+        const int g = g0 + min(i, cnt - 1);
 #pragma unroll
         for (int t = 0; t < CB; ++t) {
             qn[p][t][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -522,7 +583,7 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     // Step i: stage A(i+1), fetch A(i+2), dequantize B(i) and refill its
     // entry with group i+PB, then the MFMAs of group i.
     auto step = [&](int i, int u, bool full) {
-        if (i + 1 < ng) stage_a((u + 1) & 1);
+        if (i + 1 < cnt) stage_a((u + 1) & 1);
         load_a(i + 2);
         v4i bq[CB][4];
 #pragma unroll
@@ -535,9 +596,9 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
         if (u == 7) {
 #pragma unroll
             for (int t = 0; t < CB; ++t) rc_cur[t] = rc_next[t];
-            load_rec(rc_next, ((i + 1) >> 3) + 1);
+            load_rec(rc_next, ((g0 + i + 1) >> 3) + 1);
         }
-        if (full || i < ng) {
+        if (full || i < cnt) {
 #pragma unroll
             for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -552,8 +613,8 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     };
 
     // prologue, in steady-state issue order
-    load_rec(rc_cur, 0);
-    load_rec(rc_next, 1);
+    load_rec(rc_cur, g0 >> 3);
+    load_rec(rc_next, (g0 >> 3) + 1);
     load_a(0);
 #pragma unroll
     for (int p = 0; p < PB; ++p) load_b(p, p);
@@ -563,13 +624,28 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     constexpr int U = 8;    // unroll: one record chunk; a multiple of PB and of 2
     static_assert(U % PB == 0, "ring depth must divide the record chunk");
     int i0 = 0;
-    for (; i0 + U <= ng; i0 += U) {
+    for (; i0 + U <= cnt; i0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) step(i0 + u, u, true);
     }
-    if (i0 < ng) {
+    if (i0 < cnt) {
 #pragma unroll
         for (int u = 0; u < U; ++u) step(i0 + u, u, false);
+    }
+
+    if (part) {   // split K: the exact partial sums, 32 consecutive columns per lane group
+        int32_t* pz = part + int64_t(blockIdx.y) * M * N;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < CB; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + 32 * mt + 8 * (r >> 2) + 4 * q + (r & 3);
+                    const int n = 16 * nbw + 32 * t + j;
+                    if (m < M && n < N) pz[int64_t(m) * N + n] = acc[mt][t][r];
+                }
+        return;
     }
 
     // Epilogue through LDS: per 32-row tile, each wave converts its 32 x 32CB
@@ -937,6 +1013,14 @@ struct Args {
     int32_t* acc_debug;
 };
 
+// Second pass of a split-K launch: partial sums [splits][M][N] -> y.
+hipError_t launch_splitk_epilogue(const GemmPlan& p, const Args& a, const int32_t* part,
+                                  hipStream_t stream) {
+    const int64_t quads = int64_t(a.M) * a.N / 4;
+    return launch_kernel(splitk_epilogue_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0,
+                         stream, part, p.splits, a.M, a.N, a.s_x, a.s1, a.y, a.acc_debug);
+}
+
 template <int MT, int CB, int KW, int PD>
 hipError_t launch_decode(const GemmPlan& p, const Args& a, hipStream_t stream) {
     return launch_kernel(gemm_decode_kernel<MT, CB, KW, PD>, dim3(p.grid_x), dim3(64 * KW), 0,
@@ -945,17 +1029,26 @@ hipError_t launch_decode(const GemmPlan& p, const Args& a, hipStream_t stream) {
 }
 
 template <int MT, int CB, int NW, int P>
-hipError_t launch_lds(const GemmPlan& p, const Args& a, hipStream_t stream) {
-    return launch_kernel(gemm_lds_kernel<MT, CB, NW, P>, dim3(p.grid_x, p.grid_y), dim3(64 * NW),
-                         0, stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
-                         a.acc_debug);
+hipError_t launch_lds(const GemmPlan& p, const Args& a, void* ws, hipStream_t stream) {
+    int32_t* part = p.splits > 1 ? static_cast<int32_t*>(ws) : nullptr;
+    if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+    hipError_t e = launch_kernel(gemm_lds_kernel<MT, CB, NW, P>, dim3(p.grid_x, p.grid_y, p.splits),
+                                 dim3(64 * NW), 0, stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec,
+                                 a.ng8, a.s1, a.N, a.y, a.acc_debug, p.groups_per_split, part);
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_epilogue(p, a, part, stream);
 }
 
 template <int MT, int CB, int PB, int MINB, int NW>
-hipError_t launch_tile32(const GemmPlan& p, const Args& a, hipStream_t stream) {
-    return launch_kernel(gemm_tile32_kernel<MT, CB, PB, MINB, NW>, dim3(p.grid_x), dim3(64 * NW), 0,
-                         stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
-                         a.acc_debug);
+hipError_t launch_tile32(const GemmPlan& p, const Args& a, void* ws, hipStream_t stream) {
+    int32_t* part = p.splits > 1 ? static_cast<int32_t*>(ws) : nullptr;
+    if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+    const hipError_t e = launch_kernel(gemm_tile32_kernel<MT, CB, PB, MINB, NW>,
+                                       dim3(p.grid_x, p.splits), dim3(64 * NW), 0, stream, a.x8,
+                                       a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+                                       a.acc_debug, p.groups_per_split, part);
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_epilogue(p, a, part, stream);
 }
 
 template <int MT, int CB>
@@ -1025,18 +1118,25 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 // fail before anything is launched):
 //   M <= 64, N <= 8192:  decode family -- K split over the waves of a
 //                        workgroup, one or two column blocks per workgroup;
+//                        for 32 < M <= 64 with K >= 16384 the shared-activation
+//                        family with K split over workgroups instead;
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
-//                        LDS, waves side by side along N;
+//                        LDS, waves side by side along N (K split in two for
+//                        32 < M <= 64 and N < 32768);
 //   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
 //                        they fill whole rounds of the CUs, 128 x 256 tiles of
-//                        8 waves for short, deep shapes (N <= 8192), else
-//                        4-wave tiles sized so that ~2 workgroups per CU exist.
+//                        8 waves for short, deep shapes (N <= 8192; 128 x 512
+//                        with K in two ranges when K >= 16384), else 4-wave
+//                        tiles sized so that ~2 workgroups per CU exist, with
+//                        K split when fewer tiles than CUs remain.
+// Split K keeps INT32 partial sums [splits][M][N] in the workspace.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p{};
     const int64_t nbt = N / kBlockCols;
     const int64_t ng = K / kGroup;
     p.splits = 1;
     p.groups_per_split = int(ng);
+    p.ws_bytes = 0;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     // 32-bit buffer offsets: the fast families need the nibble and x8 buffer
     // sizes below 2^31
@@ -1045,6 +1145,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.kind = 0;
         p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         p.cb = 2;
+    } else if (M > 32 && M <= 64 && nbt >= 256 && nbt <= 512 && ng >= 128) {
+        // long K over few column blocks: the shared-activation family split
+        // over K, about one workgroup of 8 waves per CU
+        p.kind = 2; p.cb = 1; p.kw = 8; p.pd = 4;
+        p.splits = int(std::min<int64_t>(std::max<int64_t>(256 / ((nbt + 7) / 8), 1), ng / 32));
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
         if (p.mt == 1) { p.cb = 1; p.kw = 8; p.pd = 4; }
@@ -1058,8 +1163,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.kind = 2;
         p.cb = 1;
         if (nbt >= 2048) { p.kw = 12; p.pd = 2; }   // waves per workgroup, ring depth
+        else if (p.mt == 4 && ng >= 64) { p.kw = 12; p.pd = 4; p.splits = 2; }
         else { p.kw = 8; p.pd = 4; }
-        if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; }
+        if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; p.splits = 1; }
     } else {
         p.kind = 4;
         p.pa = 2;   // workgroups per CU
@@ -1071,25 +1177,38 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         // whole rounds of one wide tile per CU: the tail round is >= 90 % full
         const bool wide_fills = t_wide >= 512 && (t_wide % 256 == 0 || t_wide % 256 >= 230);
         if (wide_fills) { p.mt = 4; p.cb = 2; p.pd = 2; p.pa = 1; p.nw = 8; }
+        else if (M >= 512 && N <= 8192 && t42 >= 256 && ng >= 128) {
+            // deep and narrow: 128 x 512 tiles, K in two ranges
+            p.mt = 4; p.cb = 2; p.pd = 2; p.pa = 1; p.nw = 8; p.splits = 2;
+        }
         else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
         else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
         else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
         else { p.mt = 2; p.cb = 1; p.pd = 4; }
+        // under one workgroup per CU and a long K: split K to about two per CU
+        const int64_t tiles = ((M + 32 * p.mt - 1) / (32 * p.mt)) *
+                              ((nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw));
+        if (tiles < 256 && ng >= 64 && p.splits == 1)
+            p.splits = int(std::min<int64_t>((512 + tiles - 1) / tiles, ng / 16));
     }
     if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
         if (env[0] != '\0') {
-            int a = 0, b = 0, c = 0, d = 0, e = 4;
+            int a = 0, b = 0, c = 0, d = 0, e = 4, sp = 1;
             char fam[16] = {0};
-            const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d,%d", fam, &a, &b, &c, &d, &e);
+            const int nf =
+                std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d,%d,%d", fam, &a, &b, &c, &d, &e, &sp);
             const std::string f(fam);
             p.kind = -1;   // an override that names no compiled configuration is an error
             if (f == "decode" && nf == 5 && M <= 64 && decode_config_exists(a, b, c, d)) {
                 p.kind = 1; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
-            } else if (f == "lds" && nf == 5 && lds_config_exists(a, b, c, d)) {
+            } else if (f == "lds" && (nf == 5 || nf == 6) && lds_config_exists(a, b, c, d) &&
+                       (nf == 5 || (e >= 1 && e <= 64))) {
                 p.kind = 2; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
-            } else if (f == "tile32" && (nf == 5 || nf == 6) && small_offsets &&
-                       tile32_config_exists(a, b, c, d, e)) {
+                p.splits = nf == 6 ? e : 1;
+            } else if (f == "tile32" && (nf == 5 || nf == 6 || nf == 7) && small_offsets &&
+                       tile32_config_exists(a, b, c, d, e) && sp >= 1 && sp <= 64) {
                 p.kind = 4; p.mt = a; p.cb = b; p.pd = c; p.pa = d; p.nw = e;
+                p.splits = nf == 7 ? sp : 1;
             } else if (f == "generic" && nf >= 3 && (a == 1 || a == 2 || a == 4) && b == 2) {
                 p.kind = 0; p.mt = a; p.cb = b;
             }
@@ -1115,13 +1234,21 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.grid_x = int((nbt + 4 * p.cb - 1) / (4 * p.cb));
         p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
     }
-    p.ws_bytes = 0;
+    if (p.kind == 2 || p.kind == 4) {
+        // split K into whole record chunks of 8 groups; the partial sums
+        // [splits][M][N] live in the workspace
+        const int64_t want = std::max(1, p.splits);
+        const int64_t gps = std::min(ng, round_up((ng + want - 1) / want, 8));
+        p.groups_per_split = int(gps);
+        p.splits = int((ng + gps - 1) / gps);
+        if (p.splits > 1) p.ws_bytes = int64_t(p.splits) * M * N * 4;
+    }
     return p;
 }
 
 hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, int64_t M, int64_t K,
                        const uint8_t* packed, const uint16_t* s1, int64_t N, uint16_t* y,
-                       int32_t* acc_debug, void*, hipStream_t stream) {
+                       int32_t* acc_debug, void* ws, hipStream_t stream) {
     const PackedLayout L = packed_layout(N, K);
     const Args a{x8, s_x, int(M), int(K), packed, packed + L.rec_offset, int(L.ng8), s1, int(N),
                  y, acc_debug};
@@ -1135,14 +1262,14 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
     if (p.kind == 4) {
 #define X(A, B, C, D, E)                                                              \
     if (p.mt == A && p.cb == B && p.pd == C && p.pa == D && p.nw == E)                    \
-        return launch_tile32<A, B, C, D, E>(p, a, stream);
+        return launch_tile32<A, B, C, D, E>(p, a, ws, stream);
         QOQ_TILE32_CONFIGS(X)
 #undef X
         return hipErrorInvalidConfiguration;
     }
     if (p.kind == 2) {
 #define X(A, B, C, D) \
-    if (p.mt == A && p.cb == B && p.kw == C && p.pd == D) return launch_lds<A, B, C, D>(p, a, stream);
+    if (p.mt == A && p.cb == B && p.kw == C && p.pd == D) return launch_lds<A, B, C, D>(p, a, ws, stream);
         QOQ_LDS_CONFIGS(X)
 #undef X
         return hipErrorInvalidConfiguration;

@@ -114,11 +114,10 @@ struct GemmPlan {
     int pd;             // weight groups kept in flight per wave (register ring depth)
     int pa;             // 32x32 tile: workgroups per CU the kernel is built for
     int nw;             // 32x32 tile: waves per workgroup (side by side along N)
-    int grid_x, grid_y, splits;
-    int groups_per_split;
-    int64_t ws_acc_bytes;   // int32 partial sums
-    int64_t ws_cnt_bytes;   // arrival counters
-    int64_t ws_bytes;       // total (0 when splits == 1)
+    int grid_x, grid_y;
+    int splits;             // shared-activation family: workgroups along K (grid z)
+    int groups_per_split;   // a multiple of 8 unless it is all of K
+    int64_t ws_bytes;       // int32 partial sums [splits][M][N]; 0 when splits == 1
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);

@@ -137,12 +137,13 @@ qoq_status qoq_pack_weights(const float* W, int64_t N, int64_t K, int32_t group,
 qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K,
                             int8_t* x8, float* s_x, void* stream);
 
-/* Workspace bytes qoq_w4a8_gemm needs for this shape (0 if none). The
- * workspace holds split-K INT32 partial sums and arrival counters. It must
- * be zero-filled by the caller once, before its first use; every call that
- * completes leaves it zero-filled again, so it can be reused by later calls
- * on the same stream without clearing. Calls that overlap in time must not
- * share a workspace. Host-only. */
+/* Workspace bytes qoq_w4a8_gemm needs for this shape (0 if none). For
+ * shapes whose K is split over workgroups (long K over few output tiles) the
+ * workspace holds the exact INT32 partial sums, splits x M x N x 4 bytes;
+ * a second kernel adds them in split order and applies the epilogue. Every
+ * element is written before it is read, so no clearing is needed, and the
+ * workspace can be reused by later calls on the same stream. Calls that
+ * overlap in time must not share a workspace. Host-only. */
 size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* W4A8 GEMM (run time, the hot path).
@@ -157,14 +158,15 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   packed, s1   from qoq_pack_weights for the same N, K.
  *   y            out [M,N] fp16 bits, row-major: fp16(acc * s_x[m] * s1[n]).
  *   acc_debug    NULL, or out [M,N] int32: the exact accumulators.
- *   workspace    qoq_gemm_workspace_bytes(M, N, K) bytes (may be NULL when
- *                that is 0), zero-filled before first use (see above).
+ *   workspace    qoq_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
+ *                (may be NULL when that is 0).
  * M == 0 launches nothing.
  * Kernel choice: the library picks a kernel family and tile from (M, N, K).
  * The environment variable QOQ_GEMM_CONFIG ("decode,MT,CB,KW,PD",
- * "lds,MT,CB,NW,PD", "tile32,MT,CB,PB,WGPERCU[,NW]" or "generic,MT,2") forces one
- * compiled configuration for measurements; every configuration computes the
- * same INT32 accumulators. A value naming no compiled configuration valid
+ * "lds,MT,CB,NW,PD[,SPLITS]", "tile32,MT,CB,PB,WGPERCU[,NW[,SPLITS]]" or
+ * "generic,MT,2") forces one compiled configuration for measurements (SPLITS:
+ * K ranges over workgroups, 1..64, rounded to whole chunks of 8 groups);
+ * every configuration computes the same INT32 accumulators. A value naming no compiled configuration valid
  * for the shape makes the call fail with QOQ_ERR_CONFIG (nothing launched).
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
  * QOQ_ERR_WORKSPACE, QOQ_ERR_CONFIG, QOQ_ERR_HIP. */

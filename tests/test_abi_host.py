@@ -164,6 +164,29 @@ def test_workspace_bytes():
             assert ws >= M * 4096 * 4 and ws % 256 == 0
 
 
+def test_split_k_workspace_bytes(monkeypatch):
+    """The shared-activation family split over K keeps INT32 partial sums
+    [splits][M][N] in the workspace; ranges are whole chunks of 8 groups."""
+    for cfg, M, N, K, splits in [("lds,4,1,4,2,3", 64, 528, 2560, 3),     # 8 + 8 + 4 groups
+                                 ("lds,4,1,4,2,2", 64, 528, 2560, 2),     # 16 + 4
+                                 ("lds,4,1,4,2,64", 50, 1040, 3072, 3),   # 8 + 8 + 8
+                                 ("lds,4,1,4,2,4", 64, 528, 640, 1),      # 5 groups: one range
+                                 ("lds,4,1,4,2,1", 64, 528, 2560, 1),
+                                 ("tile32,2,1,2,2,4,3", 64, 528, 2560, 3),
+                                 ("tile32,4,1,2,1,8,2", 300, 1040, 1152, 2)]:   # 8 + 1
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+        want = splits * M * N * 4 if splits > 1 else 0
+        assert qoq.qoq_gemm_workspace_bytes(M, N, K) == want, cfg
+        # the two-call linear path carves the same partials after x8 and s_x
+        act = -(-qoq.qoq_act_bytes(M, K) // 256) * 256 + -(-4 * M // 256) * 256
+        assert qoq.qoq_linear_workspace_bytes(M, N, K) == act + want, cfg
+    for bad in ("lds,4,1,4,2,0", "lds,4,1,4,2,65", "lds,4,3,4,2,2", "tile32,2,1,2,2,4,0",
+                "tile32,2,1,2,2,4,65"):
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        assert qoq.qoq_gemm_workspace_bytes(64, 528, 2560) == 0
+        assert qoq.qoq_w4a8_gemm(P, P, 64, 2560, P, P, 528, 128, P, None, None, 0, None) == 8
+
+
 def test_pack_rejects_bad_arguments():
     f = qoq.qoq_pack_weights
     assert f(P, 4096, 4096, 64, P, P, None, 0, None) == GROUP

@@ -111,6 +111,50 @@ def test_shared_activation_family(monkeypatch, cfg):
         _run(monkeypatch, _fmt("lds", cfg), M, K, N)
 
 
+# split K: (family, config, requested splits); with K = 2560 (20 groups) a
+# request of 2 gives ranges of 16 + 4 groups, 3 or more gives 8 + 8 + 4;
+# K = 1152 gives 8 + 1; K = 640 (5 groups) stays one range
+SPLITK = [("lds", (4, 1, 4, 2), 2), ("lds", (4, 1, 4, 2), 3), ("lds", (4, 1, 8, 4), 4),
+          ("lds", (2, 1, 8, 2), 64), ("lds", (1, 1, 4, 2), 2), ("lds", (4, 2, 4, 2), 3),
+          ("lds", (4, 1, 12, 8), 2), ("tile32", (2, 1, 2, 2, 4), 3), ("tile32", (2, 1, 4, 1, 8), 2),
+          ("tile32", (4, 1, 2, 1, 8), 4), ("tile32", (1, 1, 4, 3, 4), 64),
+          ("tile32", (2, 2, 2, 2, 4), 2), ("tile32", (2, 1, 8, 2, 4), 3)]
+SPLITK_SHAPES = [(1, 2560, 208), (37, 1152, 400), (64, 2560, 528), (50, 3072, 1040), (13, 640, 208),
+                 (100, 2560, 208)]
+
+
+@pytest.mark.parametrize("fam,cfg,splits", SPLITK, ids=[_fmt(f, c) + f",{s}" for f, c, s in SPLITK])
+def test_split_k(monkeypatch, fam, cfg, splits):
+    """K split over workgroups: exact INT32 partials in the workspace, added
+    by a second kernel that applies the epilogue."""
+    name = _fmt(fam, cfg) + f",{splits}"
+    for (M, K, N) in SPLITK_SHAPES:
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", name)
+        ng = K // 128
+        gps = min(ng, -(-(-(-ng // splits)) // 8) * 8)
+        nsplit = -(-ng // gps)
+        want = nsplit * M * N * 4 if nsplit > 1 else 0
+        assert qoq.qoq_gemm_workspace_bytes(M, N, K) == want
+        _run(monkeypatch, name, M, K, N)
+
+
+def test_split_k_needs_its_workspace(monkeypatch):
+    pw, x8, s_x, _ = _case(64, 2560, 528)
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "lds,4,1,4,2,3")
+    need = qoq.qoq_gemm_workspace_bytes(64, 528, 2560)
+    assert need == 3 * 64 * 528 * 4
+    y = torch.empty((64, 528), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    st = qoq.qoq_w4a8_gemm(x8.data_ptr(), s_x.data_ptr(), 64, 2560, pw.packed.data_ptr(),
+                           pw.s1.data_ptr(), 528, 128, y.data_ptr(), None, ws.data_ptr(), need - 1,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 5                                          # QOQ_ERR_WORKSPACE
+    st = qoq.qoq_w4a8_gemm(x8.data_ptr(), s_x.data_ptr(), 64, 2560, pw.packed.data_ptr(),
+                           pw.s1.data_ptr(), 528, 128, y.data_ptr(), None, None, 0,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 5
+
+
 @pytest.mark.parametrize("cfg", TILE32, ids=[_fmt("tile32", c) for c in TILE32])
 def test_tile32_family(monkeypatch, cfg):
     for (M, K, N) in SHAPES_LARGE_M + SHAPES_SMALL_M[1:2]:

@@ -359,15 +359,28 @@ def main():
 
     # streaming-copy reference (a plain elementwise kernel: read N bytes, write
     # N bytes) of the decode weight size and of 1 GiB; its counters calibrate
-    # the HBM-traffic counters of the GEMM
+    # the HBM-traffic counters of the GEMM. The decode-size copy rotates over
+    # >= 512 MiB of buffers like the GEMM, so it reads HBM, not the cache.
     copy_ref = {}
     for label, nbytes in (("decode_weights", pw.packed.numel()), ("1GiB", 1 << 30)):
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        t = per_launch_times(torch, blocker, [lambda: torch.bitwise_not(src, out=dst)], 20)[0]
+        n = max(1, -(-ROTATE_BYTES // nbytes))
+        bufs = [(torch.empty(nbytes, dtype=torch.uint8, device=dev),
+                 torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(n)]
+        calls = [(lambda a=a, b=b: torch.bitwise_not(a, out=b)) for a, b in bufs]
+        t = per_launch_times(torch, blocker, [calls], max(20, n))[0]
         copy_ref[label] = {"bytes": nbytes, "us": round(t * 1e6, 3),
                            "gbs": round(2 * nbytes / t / 1e9, 1)}
-        del src, dst
+        del bufs, calls
+    # streaming-read reference of the decode weight size (a max-reduction
+    # reads every byte once and writes one word), same rotation
+    nbytes = pw.packed.numel()
+    n = max(1, -(-ROTATE_BYTES // nbytes))
+    rbufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(n)]
+    rcalls = [(lambda a=a: torch.amax(a)) for a in rbufs]
+    t = per_launch_times(torch, blocker, [rcalls], max(20, n))[0]
+    read_ref = {"decode_weights": {"bytes": nbytes, "us": round(t * 1e6, 3),
+                                   "gbs": round(nbytes / t / 1e9, 1)}}
+    del rbufs, rcalls
 
     # ---------------- other workloads, GEMM by GEMM ----------------
     del copies, phases, graphs
@@ -444,6 +457,7 @@ def main():
                  "weights_per_s": round(N * K / pack_t, 1),
                  "fp32_read_gbs": round(N * K * 4 / pack_t / 1e9, 1)},
         "copy_reference": copy_ref,
+        "read_reference": read_ref,
         "shapes": shapes_out,
         "variants": variants,
         "kv4_attention": kv4,

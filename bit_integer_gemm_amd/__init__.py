@@ -36,6 +36,7 @@ __all__ = [
     "w4a16_pack_weights", "w4a16_gemm",
     "kv4_cache_bytes", "kv4_alloc_cache", "kv4_smooth_factors", "kv4_append",
     "kv4_decode_attention", "kv16_alloc_cache", "kv16_append", "kv16_decode_attention",
+    "qoq_stream_read",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -134,6 +135,8 @@ def lib() -> ctypes.CDLL:
         L.qoq_w4a16_pack_weights.restype = ctypes.c_int
         L.qoq_w4a16_gemm.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         L.qoq_w4a16_gemm.restype = ctypes.c_int
+        L.qoq_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, vp]
+        L.qoq_stream_read.restype = ctypes.c_int
         L.qoq_status_string.argtypes = [ctypes.c_int]
         L.qoq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -145,6 +148,11 @@ def lib() -> ctypes.CDLL:
 # ---------------------------------------------------------------------------
 def qoq_status_string(status: int) -> str:
     return lib().qoq_status_string(int(status)).decode()
+
+
+def qoq_stream_read(buf, nbytes: int, workgroups: int, sink, stream) -> int:
+    """Measurement reference: one streaming read of `nbytes` at `buf`."""
+    return lib().qoq_stream_read(buf, nbytes, workgroups, sink, stream)
 
 
 def qoq_packed_weight_bytes(N: int, K: int, group: int = GROUP) -> int:

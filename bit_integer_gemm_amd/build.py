@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqoq.so")
-SOURCES = ["abi.hip", "pack.hip", "act_quant.hip", "gemm.hip", "variants.hip", "kv4.hip"]
+SOURCES = ["abi.hip", "pack.hip", "act_quant.hip", "gemm.hip", "variants.hip", "kv4.hip",
+           "measure.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -187,6 +187,15 @@ def test_split_k_workspace_bytes(monkeypatch):
         assert qoq.qoq_w4a8_gemm(P, P, 64, 2560, P, P, 528, 128, P, None, None, 0, None) == 8
 
 
+def test_stream_read_rejects_bad_arguments():
+    f = qoq.qoq_stream_read
+    assert f(None, 1024, 0, P, None) == NULL
+    assert f(P, 1024, 0, None, None) == NULL
+    for nbytes, wg in [(0, 0), (1000, 0), (1024, -1), (1024, 65537), ((1 << 40) + 16, 0)]:
+        assert f(P, nbytes, wg, P, None) == SHAPE, (nbytes, wg)
+    assert f(P + 8, 1024, 0, P, None) == ALIGN
+
+
 def test_pack_rejects_bad_arguments():
     f = qoq.qoq_pack_weights
     assert f(P, 4096, 4096, 64, P, P, None, 0, None) == GROUP

@@ -542,7 +542,10 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][t][r] = 0;
 
-    v4i ar[AFW];            // activation fragments of the next group to stage
+    // activation fragments of the next kAr groups to stage: group g in
+    // entry g % kAr, fetched kAr steps before it is staged
+    constexpr int kAr = 2;
+    v4i ar[kAr][AFW];
     uint4 qn[PB][CB][2];    // packed weights: group g in entry g % PB
     // group records: one 16-byte load per lane brings 8 groups of its
     // channel; the loop is unrolled by 8 so the group's slot is static
@@ -557,18 +560,18 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
 
     // i counts groups from the range start; past its end the last group is
     // loaded again (cache hits, never used)
-    auto load_a = [&](int i) {
+    auto load_a = [&](int e, int i) {
         const int g = g0 + min(i, cnt - 1);
 #pragma unroll
         for (int u = 0; u < AFW; ++u) {
             const int soff = g * kActGroupBytes + a_soff[u];
-            ar[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane[u], soff, 0));
+            ar[e][u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane[u], soff, 0));
         }
     };
-    auto stage_a = [&](int slot) {
+    auto stage_a = [&](int slot, int e) {
 #pragma unroll
         for (int u = 0; u < AFW; ++u)
-            if (owns(u)) As[slot][wave + NW * u][lane] = ar[u];
+            if (owns(u)) As[slot][wave + NW * u][lane] = ar[e][u];
     };
     auto load_b = [&](int p, int i) {
         const int g = g0 + min(i, cnt - 1);
@@ -580,11 +583,11 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
                 rb, b_lane[t], g * kBlockBytes + 512, 0));
         }
     };
-    // Step i: stage A(i+1), fetch A(i+2), dequantize B(i) and refill its
-    // entry with group i+PB, then the MFMAs of group i.
+    // Step i: stage A(i+1), fetch A(i+1+kAr) into its entry, dequantize
+    // B(i) and refill its entry with group i+PB, then the MFMAs of group i.
     auto step = [&](int i, int u, bool full) {
-        if (i + 1 < cnt) stage_a((u + 1) & 1);
-        load_a(i + 2);
+        if (i + 1 < cnt) stage_a((u + 1) & 1, (u + 1) % kAr);
+        load_a((u + 1) % kAr, i + 1 + kAr);
         v4i bq[CB][4];
 #pragma unroll
         for (int t = 0; t < CB; ++t) {
@@ -615,13 +618,14 @@ __global__ void __launch_bounds__(64 * NW, MINB) gemm_tile32_kernel(
     // prologue, in steady-state issue order
     load_rec(rc_cur, g0 >> 3);
     load_rec(rc_next, (g0 >> 3) + 1);
-    load_a(0);
+#pragma unroll
+    for (int e = 0; e < kAr; ++e) load_a(e, e);
 #pragma unroll
     for (int p = 0; p < PB; ++p) load_b(p, p);
-    stage_a(0);
-    load_a(1);
+    stage_a(0, 0);
+    load_a(0, kAr);
     __syncthreads();
-    constexpr int U = 8;    // unroll: one record chunk; a multiple of PB and of 2
+    constexpr int U = 8;    // unroll: one record chunk; a multiple of PB, 2 and kAr
     static_assert(U % PB == 0, "ring depth must divide the record chunk");
     int i0 = 0;
     for (; i0 + U <= cnt; i0 += U) {
@@ -1126,9 +1130,10 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 //   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
 //                        they fill whole rounds of the CUs, 128 x 256 tiles of
 //                        8 waves for short, deep shapes (N <= 8192; 128 x 512
-//                        with K in two ranges when K >= 16384), else 4-wave
-//                        tiles sized so that ~2 workgroups per CU exist, with
-//                        K split when fewer tiles than CUs remain.
+//                        with K in two ranges when K >= 16384), else tiles
+//                        sized so that ~2 workgroups per CU exist (down to
+//                        32 x 128 for few, short tiles), with K split when
+//                        fewer tiles than CUs remain.
 // Split K keeps INT32 partial sums [splits][M][N] in the workspace.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p{};
@@ -1183,7 +1188,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         }
         else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
         else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
-        else if (t22 >= 384) { p.mt = 2; p.cb = 2; p.pd = 2; }
+        else if (t22 >= 384) { p.mt = 2; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }   // 64 x 256, 8 waves
+        else if (((M + 63) / 64) * ((nbt + 7) / 8) < 160 && ng < 64) {
+            p.mt = 1; p.cb = 1; p.pd = 4; p.pa = 3;   // 32 x 128 tiles: twice the workgroups
+        }
         else { p.mt = 2; p.cb = 1; p.pd = 4; }
         // under one workgroup per CU and a long K: split K to about two per CU
         const int64_t tiles = ((M + 32 * p.mt - 1) / (32 * p.mt)) *

@@ -184,30 +184,46 @@ def test_zero_query_is_mean(monkeypatch):
             assert np.all(np.abs(got[b, h] - mean) <= 2.0 ** -11 * np.abs(mean) + 2.0 ** -9 * a + 1e-7)
 
 
-def test_llama_workload_sampled_heads(monkeypatch):
-    """The Llama-3-8B-shaped workload (64 sequences, 512-2048 tokens) at full
-    size, in the launch configuration the benchmark times; the oracle checks
-    a sample of (sequence, head) pairs one by one."""
+@pytest.mark.parametrize("key", list(wl.ATTN_WORKLOADS))
+def test_workload_sampled_heads(key, monkeypatch):
+    """Every attention workload the benchmark times (Llama-3-8B-shaped: 64
+    sequences of 512-2048 tokens; Qwen1.5-72B-shaped: 16 x 64 heads; long
+    contexts of 8-16 K tokens, split over workgroups) at full size, in the
+    benchmark's launch configuration, for the 4-bit and the fp16 cache; the
+    oracle checks a sample of sequences one by one."""
     monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
-    w = wl.ATTN_WORKLOADS["llama3_8b_attn"]
+    w = wl.ATTN_WORKLOADS[key]
     q, k, v, lens = wl.make_attention_case(w)
     C = int(-(-lens.max() // 32) * 32)
-    print(f"\n[gpu-case] kv4 llama workload B={w.B} C={C}", flush=True)
+    max_len = int(lens.max())
+    print(f"\n[gpu-case] kv4 workload {key} B={w.B} H={w.H} Hkv={w.H_kv} C={C}", flush=True)
     lam, lam_d = _factors(k[:4].reshape(-1, w.H_kv, D))
+    zeros = _dev(np.zeros(w.B, np.int32))
+    kd, vd = _dev(k), _dev(v)
     cache = qoq.kv4_alloc_cache(w.B, w.H_kv, C, DEV)
-    qoq.kv4_append(_dev(k), _dev(v), lam_d, _dev(np.zeros(w.B, np.int32)), cache, C)
-    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(lens), int(lens.max()), w.H_kv)
+    qoq.kv4_append(kd, vd, lam_d, zeros, cache, C)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(lens), max_len, w.H_kv)
+    del cache
+    cache16 = qoq.kv16_alloc_cache(w.B, w.H_kv, C, DEV)
+    qoq.kv16_append(kd, vd, zeros, cache16, C)
+    o16 = qoq.kv16_decode_attention(_dev(q), cache16, C, _dev(lens), max_len, w.H_kv)
     torch.cuda.synchronize()
+    del cache16, kd, vd
     got = o.cpu().float().numpy().astype(np.float64)
+    got16 = o16.cpu().float().numpy().astype(np.float64)
     G = w.H // w.H_kv
     rng = np.random.default_rng(5)
-    for b in rng.choice(w.B, 6, replace=False):
+    for b in rng.choice(w.B, min(w.B, 4), replace=False):
         n = int(lens[b])
         sub = dict(k=k[b:b + 1, :n], v=v[b:b + 1, :n])
         enc = oracle.kv4_encode(sub["k"], sub["v"], lam)
         res = oracle.kv4_decode_attention(q[b:b + 1], lam, enc, [n], G)
         tol = _tolerance(enc, res, [n])
-        assert np.all(np.abs(got[b:b + 1] - res["o"]) <= tol), b
+        assert np.all(np.abs(got[b:b + 1] - res["o"]) <= tol), ("kv4", b)
+        res16 = oracle.fp16_decode_attention(q[b:b + 1], sub["k"], sub["v"], [n], G)
+        rel = 2.0 ** -10 + (n + 64) * 2.0 ** -23 + 2.0 * (D + 8) * 2.0 ** -24 * res16["r"][0][:, None]
+        tol16 = 2.0 ** -11 * np.abs(res16["o"][0]) + rel * res16["a"][0] + 2.0 ** -24
+        assert np.all(np.abs(got16[b] - res16["o"][0]) <= tol16), ("fp16", b)
 
 
 # ---------------------------------------------------------------------------

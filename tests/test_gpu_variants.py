@@ -172,3 +172,66 @@ def test_w4a16_zero_groups_and_empty(monkeypatch):
     packed = qoq.w4a16_pack_weights(torch.from_numpy(W).to(DEV))
     e = qoq.w4a16_gemm(torch.empty((0, 512), dtype=torch.float16, device=DEV), packed, 64)
     assert e.shape == (0, 64)
+
+
+# ---------------------------------------------------------------------------
+# full-size workload shapes, sampled outputs, in the launch configurations the
+# benchmark times (each variant's default plan and the common 64 x 128 tile)
+# ---------------------------------------------------------------------------
+FULL = [("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),
+        ("qwen15_72b", "gate_up", 1024), ("qwen15_72b", "down", 1024)]
+
+
+def _sample(M, N, seed):
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.choice(N, 64, replace=False)]))
+    toks = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 48), replace=False)]))
+    return toks, cols
+
+
+def _pick(t, toks, cols):
+    ti = torch.from_numpy(toks).to(DEV)
+    ci = torch.from_numpy(cols).to(DEV)
+    return t.index_select(0, ti).index_select(1, ci).cpu().numpy()
+
+
+@pytest.mark.parametrize("key,sname,M", FULL, ids=[f"{k}-{s}-{m}" for k, s, m in FULL])
+def test_variants_full_size_sampled(key, sname, M, monkeypatch):
+    w = wl.WORKLOADS[key]
+    shp = next(s for s in w.shapes if s.name == sname)
+    K, N = shp.K, shp.N
+    W, X, _ = wl.make_case(w, shp, M)
+    toks, cols = _sample(M, N, seed=M + N)
+    Ws, Xs = W[cols], X[toks]
+    ref8 = oracle.w8a8_linear(Xs, Ws)
+    ref4 = oracle.w4a4_linear(Xs, Ws)
+    ref16 = oracle.w4a16_linear(Xs, Ws)
+    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    Wd = torch.from_numpy(W).to(DEV)
+    del W
+    xd = _half(X)
+    p8, s8 = qoq.w8a8_pack_weights(Wd)
+    p4 = qoq.w4a4_pack_weights(Wd)
+    p16 = qoq.w4a16_pack_weights(Wd)
+    del Wd
+    x8, s_x = qoq.quantize_act(xd)
+    a4 = qoq.w4a4_quantize_act(xd)
+    ng = K // 128
+    for cfg in (None, "2,1,2,2,4"):
+        if cfg:
+            monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+        print(f"\n[gpu-case] variants full {key} {sname} M={M} cfg={cfg}", flush=True)
+        y8, acc8 = qoq.w8a8_gemm(x8, s_x, p8, s8, N, acc_debug=True)
+        y4 = qoq.w4a4_gemm(a4, M, K, p4, N)
+        y16 = qoq.w4a16_gemm(xd, p16, N)
+        torch.cuda.synchronize()
+        assert np.array_equal(_pick(acc8, toks, cols).astype(np.int64), ref8["acc"]), f"w8a8 acc {cfg}"
+        yy = _pick(y8, toks, cols).astype(np.float64)
+        assert (np.abs(yy - ref8["y"]) / np.maximum(np.abs(ref8["y"]), 2.0 ** -14)).max() <= 2e-3
+        yy = _pick(y4, toks, cols).astype(np.float64)
+        tol = 2.0 ** -11 * np.abs(ref4["y"]) + (ng + 2) * 2.0 ** -22 * ref4["term_abs"] + 2.0 ** -24
+        assert not (np.abs(yy - ref4["y"]) > tol).any(), f"w4a4 {cfg}"
+        yy = _pick(y16, toks, cols).astype(np.float64)
+        tol = 2.0 ** -11 * np.abs(ref16["y"]) + (K + 2) * 2.0 ** -23 * ref16["term_abs"] + 2.0 ** -24
+        assert not (np.abs(yy - ref16["y"]) > tol).any(), f"w4a16 {cfg}"
+        monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)

@@ -217,14 +217,23 @@ def test_workspace_is_reusable():
 # ---------------------------------------------------------------------------
 CASES = [(key, shape.name, M) for key in wl.ORDER[1:] for shape in wl.WORKLOADS[key].shapes
          for M in wl.WORKLOADS[key].Ms]
+COMMON_TILE_CASES = {("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),
+                     ("qwen15_72b", "gate_up", 1024), ("qwen15_72b", "down", 1024)}
 
 
 @pytest.mark.parametrize("key,shape_name,M", CASES, ids=[f"{k}-{s}-M{m}" for k, s, m in CASES])
-def test_workload_full_size_sampled(key, shape_name, M):
+def test_workload_full_size_sampled(key, shape_name, M, monkeypatch):
     w = wl.WORKLOADS[key]
     shape = next(s for s in w.shapes if s.name == shape_name)
     _announce("workload", key, shape_name, M, shape.K, shape.N)
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
     W, X, _ = wl.make_case(w, shape, M)
     pw, x8, s_x, y, acc = gpu_run(W, X)
     err = sampled_check(W, X, pw, x8, s_x, y, acc)
     print(f"[gpu-case] ok max rel err {err:.2e}", flush=True)
+    if (key, shape_name, M) in COMMON_TILE_CASES:
+        # the benchmark's format comparison also times the common 64 x 128 tile
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", "tile32,2,1,2,2,4")
+        y2, acc2 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+        torch.cuda.synchronize()
+        sampled_check(W, X, pw, x8, s_x, y2, acc2)

@@ -462,20 +462,25 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
             }
         }
         const v8h pop = softmax(zs);
-        // values: (1024 + u) - (1024 + z) = u - z exactly, times s (one
-        // rounding); tokens past the context get scale 0 and a neutral zero
-        h2 zz[4], ss[4];
+        // values: sum_t p_t s_t (u_t - z_t). The token's scale rides on its
+        // probability, P' = fp16(fp16(p) s) (tokens past the context get
+        // scale 0, whatever bits their slot holds), and the value operand is
+        // the exact integer (1024 + u) - (1024 + z) = u - z: one packed
+        // subtraction per two values, no per-value scaling.
         const uint32_t svw[4] = {r.sv.x, r.sv.y, r.sv.z, r.sv.w};
         // 1024 + z_v pairs: the zero bytes with 0x64 exponent bytes between
-        const uint32_t zvw[4] = {__builtin_amdgcn_perm(c64, zv03, 0x04010400u),
-                                 __builtin_amdgcn_perm(c64, zv03, 0x04030402u),
-                                 __builtin_amdgcn_perm(c64, zv47, 0x04010400u),
-                                 __builtin_amdgcn_perm(c64, zv47, 0x04030402u)};
+        h2 zz[4];
+        zz[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, zv03, 0x04010400u));
+        zz[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, zv03, 0x04030402u));
+        zz[2] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, zv47, 0x04010400u));
+        zz[3] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, zv47, 0x04030402u));
+        v8h pv;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
             const uint32_t keep = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
-            ss[pr] = __builtin_bit_cast(h2, svw[pr] & keep);
-            zz[pr] = __builtin_bit_cast(h2, (zvw[pr] & keep) | (0x64006400u & ~keep));
+            const h2 ps = h2{pop[2 * pr], pop[2 * pr + 1]} * __builtin_bit_cast(h2, svw[pr] & keep);
+            pv[2 * pr] = ps[0];
+            pv[2 * pr + 1] = ps[1];
         }
         const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
 #pragma unroll
@@ -483,8 +488,8 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
             h2 u[4];
             unpack_1024(vw[c], nib, e64, u);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u[i] = (u[i] - zz[i]) * ss[i];
-            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pop, o[c], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) u[i] = u[i] - zz[i];
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pv, o[c], 0, 0, 0);
         }
     };
     auto compute = [&](const Blk& r, int blk) {

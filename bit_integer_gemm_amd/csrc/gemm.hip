@@ -1122,11 +1122,12 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 // fail before anything is launched):
 //   M <= 64, N <= 8192:  decode family -- K split over the waves of a
 //                        workgroup, one or two column blocks per workgroup;
-//                        for 32 < M <= 64 with K >= 16384 the shared-activation
-//                        family with K split over workgroups instead;
+//                        for 32 < M <= 64, N >= 4096 and K >= 16384 the
+//                        shared-activation family with K split over
+//                        workgroups instead;
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
 //                        LDS, waves side by side along N (K split in two for
-//                        32 < M <= 64 and N < 32768);
+//                        32 < M <= 64, N < 32768 and K >= 8192);
 //   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
 //                        they fill whole rounds of the CUs, 128 x 256 tiles of
 //                        8 waves for short, deep shapes (N <= 8192; 128 x 512

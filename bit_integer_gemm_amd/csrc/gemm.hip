@@ -1169,7 +1169,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.kind = 2;
         p.cb = 1;
         if (nbt >= 2048) { p.kw = 12; p.pd = 2; }   // waves per workgroup, ring depth
-        else if (p.mt == 4 && ng >= 64) { p.kw = 12; p.pd = 4; p.splits = 2; }
+        else if (p.mt == 4 && ng >= 64) { p.kw = 16; p.pd = 2; p.splits = 2; }
         else { p.kw = 8; p.pd = 4; }
         if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; p.splits = 1; }
     } else {

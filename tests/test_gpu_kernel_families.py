@@ -116,7 +116,7 @@ def test_shared_activation_family(monkeypatch, cfg):
 # K = 1152 gives 8 + 1; K = 640 (5 groups) stays one range
 SPLITK = [("lds", (4, 1, 4, 2), 2), ("lds", (4, 1, 4, 2), 3), ("lds", (4, 1, 8, 4), 4),
           ("lds", (2, 1, 8, 2), 64), ("lds", (1, 1, 4, 2), 2), ("lds", (4, 2, 4, 2), 3),
-          ("lds", (4, 1, 12, 8), 2), ("tile32", (2, 1, 2, 2, 4), 3), ("tile32", (2, 1, 4, 1, 8), 2),
+          ("lds", (4, 1, 12, 8), 2), ("lds", (4, 1, 16, 2), 2), ("tile32", (2, 1, 2, 2, 4), 3), ("tile32", (2, 1, 4, 1, 8), 2),
           ("tile32", (4, 1, 2, 1, 8), 4), ("tile32", (1, 1, 4, 3, 4), 64),
           ("tile32", (2, 2, 2, 2, 4), 2), ("tile32", (2, 1, 8, 2, 4), 3)]
 SPLITK_SHAPES = [(1, 2560, 208), (37, 1152, 400), (64, 2560, 528), (50, 3072, 1040), (13, 640, 208),

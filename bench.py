@@ -224,8 +224,9 @@ def traffic_record():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the sharding plan is in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(the GEMM would shard by output columns, or by K with an exact INT32 sum); "
+              "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import bit_integer_gemm_amd as qoq

@@ -3,7 +3,7 @@
  * Not part of the quantized GEMM. It gives the bandwidth one kernel launch
  * achieves on this GPU for a buffer of a given size, the reference against
  * which the weight-streaming GEMM kernels of small batches (a few MB read in
- * a few microseconds, where the launch ramp dominates) are judged. */
+ * a few microseconds, where the launch ramp dominates) are compared. */
 #ifndef QOQ_MEASURE_H
 #define QOQ_MEASURE_H
 

@@ -258,29 +258,43 @@ struct AttnArgs {
     float* part;               // [B, H, splits, D + 2] when splits > 1
     int64_t C;
     int B, H, Hkv, G, splits, bps, max_len;
+    int paired;                // 1: workgroup p takes the KV head's contexts of length
+                               // ranks p and B - 1 - p (splits == 1, B <= kPairMaxB)
 };
 
-// One workgroup (4 waves) per (sequence, KV head, split). Wave w takes the
-// split's blocks w, w + 4, ...; per block: 2 score MFMAs tiles x 4 steps
-// (tokens x queries), online softmax per query, 8 value MFMAs (dims x
-// queries). The four waves' states are merged in LDS at the end.
+// Largest batch the paired schedule ranks in LDS.
+constexpr int kPairMaxB = 256;
+
+// One workgroup (NW = 4 or 8 waves) per (sequence, KV head, split), or, in
+// the paired schedule, per (pair of sequences, KV head): the sequences are
+// ranked by context length in the workgroup (ties by index) and workgroup p
+// takes ranks p and B - 1 - p one after the other, so every workgroup holds
+// about the same number of tokens and none waits for the longest context
+// alone. Wave w takes the blocks w, w + NW, ...; per block: 2 score MFMAs
+// tiles x 4 steps (tokens x queries), online softmax per query, 8 value
+// MFMAs (dims x queries). The waves' states are merged in LDS at the end of
+// each context.
 // kF16: the same kernel on an fp16 cache (the comparison point for what the
 // 4-bit cache buys): keys and values are the MFMA operands as stored, the
 // query is used unsmoothed, nothing is dequantized. Per 32-token block the
 // fp16 layout holds keys [tile 2][g 4][t 16][st 4][8 halves] and values
 // [g 4][d 16][c 8][8 halves] (tokens pi(8 g + e)), 8 KiB each.
-template <bool kF16>
-__global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
+template <bool kF16, int NW>
+__global__ void __launch_bounds__(64 * NW) kv4_attention_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15;          // query of the group (MFMA column)
     const int g = lane >> 4;          // lane group
-    const int sp = blockIdx.x % a.splits;
-    const int region = blockIdx.x / a.splits;
-    const int h = region % a.Hkv;
-    const int b = region / a.Hkv;
     const int64_t C = a.C;
-    const int len = int(min(int64_t(max(min(a.lens[b], a.max_len), 0)), C));
+    __shared__ float sm[NW][16], sl[NW][16];
+    __shared__ float so[NW][16][kD + 4];
+    __shared__ int rank_len[kPairMaxB], by_rank[kPairMaxB];
+    auto clamped_len = [&](int b) { return int(min(int64_t(max(min(a.lens[b], a.max_len), 0)), C)); };
+
+  // one (sequence, KV head, split): the whole attention of its queries
+  auto run = [&](const int b, const int h, const int sp) {
+    const int region = b * a.Hkv + h;
+    const int len = clamped_len(b);
     const int nb = (len + kBlk - 1) / kBlk;
     const int blk0 = sp * a.bps;
     const int blk1 = min(nb, blk0 + a.bps);
@@ -497,24 +511,22 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
         else compute4(r, blk);
     };
 
-    // the wave's blocks: blk0 + wave, + 4, ...; the next block's loads are
+    // the wave's blocks: blk0 + wave, + NW, ...; the next block's loads are
     // in flight while one is computed
     Blk ra, rb;
     int bi = blk0 + wave;
     if (bi < blk1) load(ra, bi);
-    for (; bi < blk1; bi += 8) {
-        if (bi + 4 < blk1) load(rb, bi + 4);
+    for (; bi < blk1; bi += 2 * NW) {
+        if (bi + NW < blk1) load(rb, bi + NW);
         compute(ra, bi);
-        if (bi + 4 >= blk1) break;
-        if (bi + 8 < blk1) load(ra, bi + 8);
-        compute(rb, bi + 4);
+        if (bi + NW >= blk1) break;
+        if (bi + 2 * NW < blk1) load(ra, bi + 2 * NW);
+        compute(rb, bi + NW);
     }
 
-    // merge the four waves: lane (j, g) holds query j, dims 16 c + 4 g + i
+    // merge the waves: lane (j, g) holds query j, dims 16 c + 4 g + i
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    __shared__ float sm[4][16], sl[4][16];
-    __shared__ float so[4][16][kD + 4];
     if (g == 0) {
         sm[wave][j] = m;
         sl[wave][j] = l;
@@ -524,16 +536,17 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) so[wave][j][16 * c + 4 * g + i] = o[c][i];
     __syncthreads();
-    // thread -> (query jq, 8 dims); 16 queries x 128 dims / 256 threads
+    // thread -> (query jq, 8 dims); 16 queries x 128 dims over the first
+    // 256 threads (G <= 16: the others hold no query)
     const int jq = threadIdx.x >> 4;
     const int d0 = (threadIdx.x & 15) * 8;
     if (jq >= a.G) return;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][jq]);
-    float L = 0.0f, f[4];
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][jq]);
+    float L = 0.0f, f[NW];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
         f[w] = M == -INFINITY ? 0.0f : exp2f(sm[w][jq] - M);
         L += f[w] * sl[w][jq];
     }
@@ -542,7 +555,7 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) {
         acc[e] = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[e] += f[w] * so[w][jq][d0 + e];
+        for (int w = 0; w < NW; ++w) acc[e] += f[w] * so[w][jq][d0 + e];
     }
     const int64_t row = int64_t(b) * a.H + h * a.G + jq;
     if (a.splits == 1) {
@@ -563,6 +576,34 @@ __global__ void __launch_bounds__(256) kv4_attention_kernel(AttnArgs a) {
             pp[kD] = M;
             pp[kD + 1] = L;
         }
+    }
+  };
+
+    if (!a.paired) {
+        const int region = blockIdx.x / a.splits;
+        run(region / a.Hkv, region % a.Hkv, blockIdx.x % a.splits);
+        return;
+    }
+    // paired schedule: rank the contexts by length (longest first, ties by
+    // index), then take ranks p and B - 1 - p
+    for (int t = threadIdx.x; t < a.B; t += 64 * NW) rank_len[t] = clamped_len(t);
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.B; t += 64 * NW) {
+        const int lt = rank_len[t];
+        int r = 0;
+        for (int u = 0; u < a.B; ++u) {
+            const int lu = rank_len[u];
+            r += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+        }
+        by_rank[r] = t;
+    }
+    __syncthreads();
+    const int p = blockIdx.x / a.Hkv;
+    const int h = blockIdx.x % a.Hkv;
+    run(by_rank[p], h, 0);
+    if (a.B - 1 - p != p) {
+        __syncthreads();   // the merge buffers are reused
+        run(by_rank[a.B - 1 - p], h, 0);
     }
 }
 
@@ -631,7 +672,9 @@ int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C) { return B * Hkv * C 
 // a second kernel. (Measured on MI355X: cutting every context into fixed
 // 256-1024-token splits to even out ragged lengths is slower -- the
 // per-workgroup query set-up and merge cost more than the imbalance.)
-// QOQ_KV4_SPLITS=<n> forces n splits.
+// QOQ_KV4_SPLITS=<n> forces n splits. Unsplit batches of 2..256 sequences
+// whose pairs fit one per CU take the paired schedule (8-wave workgroups);
+// QOQ_KV4_PAIRED=0 turns it off.
 Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     Kv4Plan p{};
     const int64_t nb = std::max<int64_t>(1, (max_len + kBlk - 1) / kBlk);
@@ -645,6 +688,17 @@ Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     p.splits = int(splits);
     p.bps = int(std::max<int64_t>(1, (nb + splits - 1) / splits));
     p.grid = B * Hkv * splits;
+    p.waves = 4;
+    // pairs as 8-wave workgroups, at most one per CU (more pairs than CUs
+    // would run two contexts back to back per 4-wave workgroup, which costs
+    // the fp16 cache more than it saves: 121 -> 133 us on 16 x 64 heads)
+    p.paired = splits == 1 && B >= 2 && B <= kPairMaxB && (B + 1) / 2 * Hkv <= 256;
+    if (const char* env = std::getenv("QOQ_KV4_PAIRED"))
+        if (env[0] == '0') p.paired = false;
+    if (p.paired) {
+        p.grid = (B + 1) / 2 * Hkv;
+        p.waves = 8;
+    }
     return p;
 }
 
@@ -673,14 +727,22 @@ int64_t kv4_workspace_bytes(const Kv4Plan& p, int64_t B, int64_t H) {
     return p.splits > 1 ? B * H * p.splits * (kD + 4) * int64_t(sizeof(float)) : 0;
 }
 
+template <bool kF16>
+hipError_t launch_attention_kernel(const Kv4Plan& p, const AttnArgs& a, hipStream_t stream) {
+    if (p.waves == 8)
+        return launch_kernel(kv4_attention_kernel<kF16, 8>, dim3(unsigned(p.grid)), dim3(512), 0,
+                             stream, a);
+    return launch_kernel(kv4_attention_kernel<kF16, 4>, dim3(unsigned(p.grid)), dim3(256), 0,
+                         stream, a);
+}
+
 hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,
                                 int64_t Hkv, const uint16_t* lam, const uint8_t* cache, int64_t C,
                                 const int32_t* lens, int64_t max_len, uint16_t* out, float* part,
                                 hipStream_t stream) {
     AttnArgs a{q, lam, cache, lens, out, part, C, int(B), int(H), int(Hkv), int(H / Hkv), p.splits,
-               p.bps, int(max_len)};
-    hipError_t e = launch_kernel(kv4_attention_kernel<false>, dim3(unsigned(p.grid)), dim3(256), 0,
-                                 stream, a);
+               p.bps, int(max_len), p.paired ? 1 : 0};
+    hipError_t e = launch_attention_kernel<false>(p, a, stream);
     if (e != hipSuccess || p.splits == 1) return e;
     const int rows = int(B * H);
     return launch_kernel(kv4_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,
@@ -702,9 +764,8 @@ hipError_t launch_kv16_attention(const Kv4Plan& p, const uint16_t* q, int64_t B,
                                  int64_t Hkv, const uint8_t* cache, int64_t C, const int32_t* lens,
                                  int64_t max_len, uint16_t* out, float* part, hipStream_t stream) {
     AttnArgs a{q, nullptr, cache, lens, out, part, C, int(B), int(H), int(Hkv), int(H / Hkv),
-               p.splits, p.bps, int(max_len)};
-    hipError_t e = launch_kernel(kv4_attention_kernel<true>, dim3(unsigned(p.grid)), dim3(256), 0,
-                                 stream, a);
+               p.splits, p.bps, int(max_len), p.paired ? 1 : 0};
+    hipError_t e = launch_attention_kernel<true>(p, a, stream);
     if (e != hipSuccess || p.splits == 1) return e;
     const int rows = int(B * H);
     return launch_kernel(kv4_combine_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,

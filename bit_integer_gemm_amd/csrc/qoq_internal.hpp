@@ -180,6 +180,8 @@ hipError_t launch_w4a4_gemm(const VariantPlan& p, const uint8_t* act, int64_t M,
 struct Kv4Plan {
     int splits;        // workgroups per (sequence, KV head), context split evenly
     int bps;           // 32-token blocks per split
+    int waves;         // waves per workgroup (4 or 8)
+    bool paired;       // workgroups take two sequences of complementary length rank
     int64_t grid;
 };
 int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C);

@@ -9,6 +9,7 @@ give 0); every split of the contexts; the full Llama-3-8B-shaped workload on
 sampled heads.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -99,7 +100,8 @@ def _run(B, H, Hkv, lens, C, seed, monkeypatch, splits=None, chunks=None):
     monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
     if splits:
         monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
-    print(f"\n[gpu-case] kv4 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits}",
+    print(f"\n[gpu-case] kv4 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits} "
+          f"paired={os.environ.get('QOQ_KV4_PAIRED', 'default')}",
           flush=True)
     q, k, v, lam, lam_d, cache = _build(B, H, Hkv, lens, C, seed, chunks)
     T = k.shape[1]
@@ -136,6 +138,23 @@ def test_smooth_factors_exact():
 ])
 def test_attention_parity(B, H, Hkv, lens, C, monkeypatch):
     got, res, _ = _run(B, H, Hkv, lens, C, seed=B + H + C, monkeypatch=monkeypatch)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("paired", ["1", "0"])
+@pytest.mark.parametrize("B,H,Hkv,lens,C", [
+    (5, 8, 2, [40, 128, 3, 128, 77], 128),     # odd batch (the middle rank runs alone), a tie
+    (6, 4, 1, [0, 96, 1, 64, 95, 96], 96),      # empty context, ties, one-token context
+    (2, 32, 8, [128, 17], 128),                 # one pair
+])
+def test_paired_schedule(B, H, Hkv, lens, C, paired, monkeypatch):
+    """Unsplit batches of 2..256 sequences whose pairs fit one per CU run two
+    contexts of complementary length rank per 8-wave workgroup; the same
+    cases with the schedule turned off meet the same bound."""
+    monkeypatch.setenv("QOQ_KV4_PAIRED", paired)
+    got, res, _ = _run(B, H, Hkv, lens, C, seed=B + 3 * H + C, monkeypatch=monkeypatch)
     for b, n in enumerate(lens):
         if n == 0:
             assert np.all(got[b] == 0)
@@ -233,7 +252,8 @@ def _run16(B, H, Hkv, lens, C, seed, monkeypatch, splits=None):
     monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
     if splits:
         monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
-    print(f"\n[gpu-case] kv16 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits}",
+    print(f"\n[gpu-case] kv16 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits} "
+          f"paired={os.environ.get('QOQ_KV4_PAIRED', 'default')}",
           flush=True)
     q, k, v = wl.make_attention(B, H, Hkv, D, lens, seed=seed)
     cache = qoq.kv16_alloc_cache(B, Hkv, C, DEV)
@@ -261,6 +281,12 @@ def test_fp16_attention_parity(B, H, Hkv, lens, C, monkeypatch):
     for b, n in enumerate(lens):
         if n == 0:
             assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("paired", ["1", "0"])
+def test_fp16_paired_schedule(paired, monkeypatch):
+    monkeypatch.setenv("QOQ_KV4_PAIRED", paired)
+    _run16(5, 8, 2, [40, 128, 3, 128, 77], 128, seed=31, monkeypatch=monkeypatch)
 
 
 @pytest.mark.parametrize("splits", [2, 5])

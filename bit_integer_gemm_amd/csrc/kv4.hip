@@ -608,10 +608,10 @@ __global__ void __launch_bounds__(64 * NW) kv4_attention_kernel(AttnArgs a) {
 }
 
 // Splits of one (sequence, query head) merged: one wave, 2 dims per lane;
-// only the splits that hold tokens of the sequence are read. Lane s reads
-// split s's maximum and sum (one round trip for all splits), the weights
-// come from wave reductions, and the partial outputs are read eight splits
-// at a time with independent loads.
+// only the splits that hold tokens of the sequence are read. Up to 16 of
+// them, every load is issued at once (one round trip); beyond that, lane s
+// reads split s's maximum and sum, the weights come from wave reductions,
+// and the partial outputs are read eight splits at a time.
 __global__ void __launch_bounds__(256) kv4_combine_kernel(const float* __restrict__ part, int rows,
                                                           int H, int splits, int bps,
                                                           const int32_t* __restrict__ lens,
@@ -625,6 +625,36 @@ __global__ void __launch_bounds__(256) kv4_combine_kernel(const float* __restric
     const int nb = (len + kBlk - 1) / kBlk;
     const int ns = min(splits, (nb + bps - 1) / bps);
     const float* pp = part + int64_t(row) * splits * (kD + 4);
+    if (ns >= 1 && ns <= 16) {
+        // up to 16 splits: every load (each split's maximum and sum, and the
+        // lane's two dims of each partial output) in one round trip
+        float2 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            v[u] = *reinterpret_cast<const float2*>(pp + int64_t(min(u, ns - 1)) * (kD + 4) + 2 * lane);
+        const float* q = pp + int64_t(min(lane, ns - 1)) * (kD + 4);
+        const float mz = lane < ns ? q[kD] : -INFINITY;
+        const float lz = q[kD + 1];
+        float M = mz;
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+        const float f = lane < ns ? exp2f(mz - M) : 0.0f;
+        float L = f * lz;
+        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+        float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float fu = __shfl(f, u, 64);
+            if (u < ns) {
+                o0 += fu * v[u].x;
+                o1 += fu * v[u].y;
+            }
+        }
+        const float x0 = L > 0.0f ? o0 / L : 0.0f, x1 = L > 0.0f ? o1 / L : 0.0f;
+        *reinterpret_cast<uint32_t*>(out + int64_t(row) * kD + 2 * lane) =
+            uint32_t(__half_as_ushort(__float2half_rn(x0))) |
+            (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+        return;
+    }
     float M = -INFINITY;
     for (int s0 = 0; s0 < ns; s0 += 64)
         if (s0 + lane < ns) M = fmaxf(M, pp[int64_t(s0 + lane) * (kD + 4) + kD]);

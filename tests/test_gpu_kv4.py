@@ -160,6 +160,12 @@ def test_paired_schedule(B, H, Hkv, lens, C, paired, monkeypatch):
             assert np.all(got[b] == 0)
 
 
+def test_many_splits_merge(monkeypatch):
+    """More than 16 splits of one context (one block each): the merge reads
+    its splits in rounds of eight instead of all at once."""
+    _run(2, 8, 2, [600, 100], 640, seed=19, monkeypatch=monkeypatch, splits=32)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
 def test_attention_every_split(splits, monkeypatch):
     _run(3, 8, 2, [300, 45, 257], 320, seed=17, monkeypatch=monkeypatch, splits=splits)

@@ -196,6 +196,21 @@ def test_stream_read_rejects_bad_arguments():
     assert f(P + 8, 1024, 0, P, None) == ALIGN
 
 
+def test_default_plans_split_long_k(monkeypatch):
+    """The planner splits K for long-K shapes over few output tiles (the
+    workspace then holds splits x M x N INT32 partials) and nowhere else."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    ws = qoq.qoq_gemm_workspace_bytes
+    assert ws(64, 8192, 24576) == 4 * 64 * 8192 * 4          # Qwen1.5-72B down, M = 64
+    assert ws(64, 24576, 8192) == 2 * 64 * 24576 * 4         # Qwen1.5-72B qkv, M = 64
+    assert ws(256, 4096, 14336) == 4 * 256 * 4096 * 4        # Llama-3-8B down, M = 256
+    assert ws(1024, 8192, 24576) == 2 * 1024 * 8192 * 4      # Qwen1.5-72B down, M = 1024
+    for M, N, K in [(1, 4096, 4096), (8, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
+                    (64, 49152, 8192), (256, 6144, 4096), (256, 4096, 4096), (256, 28672, 4096),
+                    (4096, 14336, 4096), (1024, 49152, 8192), (1024, 24576, 8192), (16, 512, 512)]:
+        assert ws(M, N, K) == 0, (M, N, K)
+
+
 def test_pack_rejects_bad_arguments():
     f = qoq.qoq_pack_weights
     assert f(P, 4096, 4096, 64, P, P, None, 0, None) == GROUP

@@ -156,6 +156,43 @@ def test_identity_canonical_packing():
         check_y(y.cpu().numpy().astype(np.float64), oracle.epilogue(want, sx_ref, s1))
 
 
+def test_offsets_beyond_2_31():
+    """The largest shapes: 2^32 weights (2 GiB of packed nibbles), so byte
+    offsets pass 2^31 and the plan takes the 64-bit generic kernel. Codes are
+    packed from canonical form (s2 = 1, random zeros) generated on the GPU;
+    the oracle checks sampled output channels for M = 1 and a ragged M = 20."""
+    N, K = 32768, 131072
+    assert qoq.qoq_packed_weight_bytes(N, K) > (1 << 31)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    q4 = torch.randint(0, 16, (N, K), dtype=torch.uint8, device=DEV, generator=g)
+    z = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=DEV, generator=g)
+    s2 = torch.ones((N, K // 128), dtype=torch.int8, device=DEV)
+    s1 = (torch.rand(N, device=DEV, generator=g) * 0.01 + 0.001).to(torch.float16)
+    pw = qoq.pack_canonical(q4, s2, z, s1)
+    rng = np.random.default_rng(13)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 46, replace=False)]))
+    ci = torch.from_numpy(cols).to(DEV)
+    w8 = oracle.dequantize_level2(q4.index_select(0, ci).cpu().numpy(),
+                                  s2.index_select(0, ci).cpu().numpy(),
+                                  z.index_select(0, ci).cpu().numpy(), 128)
+    s1_s = s1.index_select(0, ci).cpu().numpy()
+    del q4
+    for M in (1, 20):
+        _announce("offsets beyond 2^31", M, K, N)
+        _, X, _ = wl.make_inputs(M, K, 16, seed=M)
+        x8, s_x = qoq.quantize_act(torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV))
+        y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+        torch.cuda.synchronize()
+        x8_ref, sx_ref = oracle.quantize_act(X)
+        assert np.array_equal(act_rows(x8, M), x8_ref)
+        want = x8_ref.astype(np.int64) @ w8.astype(np.int64).T
+        got = acc.index_select(1, ci).cpu().numpy().astype(np.int64)
+        assert np.array_equal(got, want)
+        check_y(y.index_select(1, ci).cpu().numpy().astype(np.float64),
+                oracle.epilogue(want, sx_ref, s1_s))
+
+
 def test_hand_cases_padded():
     """The hand-worked groups, zero-padded to 128 inputs (padding with zero
     changes no group parameter), through the GPU path."""

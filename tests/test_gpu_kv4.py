@@ -118,6 +118,46 @@ def _run(B, H, Hkv, lens, C, seed, monkeypatch, splits=None, chunks=None):
     return got, res, ref
 
 
+@pytest.mark.parametrize("fp16", [False, True])
+def test_cache_offsets_beyond_2_32(fp16, monkeypatch):
+    """A cache of 2^21 tokens per (sequence, KV head): the last regions start
+    more than 4 GiB into the buffer (64-bit region offsets); short contexts
+    keep the oracle small. Appended at the start of every region and, for the
+    second sequence, at the far end of its capacity."""
+    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    B, H, Hkv, C = 2, 32, 8, 1 << 21
+    lens = np.array([50, 77], np.int32)
+    print(f"\n[gpu-case] kv{'16' if fp16 else '4'} capacity 2^21 B={B} Hkv={Hkv}", flush=True)
+    q, k, v = wl.make_attention(B, H, Hkv, D, lens, seed=23)
+    lam, lam_d = _factors(k.reshape(-1, Hkv, D))
+    if fp16:
+        cache = qoq.kv16_alloc_cache(B, Hkv, C, DEV)
+        assert cache.numel() > (1 << 33)
+        qoq.kv16_append(_dev(k), _dev(v), _dev(np.zeros(B, np.int32)), cache, C)
+        # the same tokens again at the far end of the capacity (never read)
+        qoq.kv16_append(_dev(k), _dev(v), _dev(np.full(B, C - k.shape[1], np.int32)), cache, C)
+        o = qoq.kv16_decode_attention(_dev(q), cache, C, _dev(lens), int(lens.max()), Hkv)
+        res = oracle.fp16_decode_attention(q, k, v, lens, H // Hkv)
+        torch.cuda.synchronize()
+        got = o.cpu().float().numpy().astype(np.float64)
+        for b, n in enumerate(lens):
+            rel = 2.0 ** -10 + (n + 64) * 2.0 ** -23 + 2.0 * (D + 8) * 2.0 ** -24 * res["r"][b][:, None]
+            tol = 2.0 ** -11 * np.abs(res["o"][b]) + rel * res["a"][b] + 2.0 ** -24
+            assert np.all(np.abs(got[b] - res["o"][b]) <= tol), b
+        return
+    cache = qoq.kv4_alloc_cache(B, Hkv, C, DEV)
+    assert cache.numel() > (1 << 32)
+    qoq.kv4_append(_dev(k), _dev(v), lam_d, _dev(np.zeros(B, np.int32)), cache, C)
+    qoq.kv4_append(_dev(k), _dev(v), lam_d, _dev(np.full(B, C - k.shape[1], np.int32)), cache, C)
+    o = qoq.kv4_decode_attention(_dev(q), lam_d, cache, C, _dev(lens), int(lens.max()), Hkv)
+    torch.cuda.synchronize()
+    enc = oracle.kv4_encode(k, v, lam)
+    res = oracle.kv4_decode_attention(q, lam, enc, lens, H // Hkv)
+    got = o.cpu().float().numpy().astype(np.float64)
+    tol = _tolerance(enc, res, lens)
+    assert np.all(np.abs(got - res["o"]) <= tol)
+
+
 def test_smooth_factors_exact():
     rng = np.random.default_rng(3)
     kc = (rng.standard_normal((300, 4, D)) * np.exp(rng.standard_normal((1, 4, D)))).astype(np.float16)

@@ -280,7 +280,8 @@ constexpr int kPairMaxB = 256;
 // fp16 layout holds keys [tile 2][g 4][t 16][st 4][8 halves] and values
 // [g 4][d 16][c 8][8 halves] (tokens pi(8 g + e)), 8 KiB each.
 template <bool kF16, int NW>
-__global__ void __launch_bounds__(64 * NW) kv4_attention_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kF16 ? 1 : 3)))
+kv4_attention_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15;          // query of the group (MFMA column)

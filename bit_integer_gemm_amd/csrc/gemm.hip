@@ -1128,6 +1128,7 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
 //                        LDS, waves side by side along N (K split in two for
 //                        32 < M <= 64, N < 32768 and K >= 8192);
+//   64 < M <= 256, N <= 4096, K <= 4096: decode family, 64-row tiles;
 //   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
 //                        they fill whole rounds of the CUs, 128 x 256 tiles of
 //                        8 waves for short, deep shapes (N <= 8192; 128 x 512
@@ -1165,6 +1166,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         else { p.cb = 1; p.kw = 8; p.pd = 4; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
+    } else if (M > 64 && M <= 256 && nbt <= 256 && ng <= 32 && nbt % 16 == 0) {
+        // short, narrow layers at a few hundred tokens (Llama-3-8B o at
+        // M = 256): the decode family's K-split waves over 64-row tiles beat
+        // the 32x32 tiles, which leave half the CUs with one wave per SIMD
+        p.kind = 1; p.mt = 4; p.cb = 2; p.kw = 4; p.pd = 2;
     } else if (M <= 64) {
         p.kind = 2;
         p.cb = 1;
@@ -1208,7 +1214,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
                 std::sscanf(env, "%15[a-z0-9],%d,%d,%d,%d,%d,%d", fam, &a, &b, &c, &d, &e, &sp);
             const std::string f(fam);
             p.kind = -1;   // an override that names no compiled configuration is an error
-            if (f == "decode" && nf == 5 && M <= 64 && decode_config_exists(a, b, c, d)) {
+            if (f == "decode" && nf == 5 && M <= 256 && decode_config_exists(a, b, c, d)) {
                 p.kind = 1; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
             } else if (f == "lds" && (nf == 5 || nf == 6) && lds_config_exists(a, b, c, d) &&
                        (nf == 5 || (e >= 1 && e <= 64))) {

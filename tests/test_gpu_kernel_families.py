@@ -95,6 +95,22 @@ def test_decode_family_row_tiles(monkeypatch, cfg):
             _run(monkeypatch, _fmt("decode", cfg), M, 1152, N)
 
 
+@pytest.mark.parametrize("M,K,N", [(200, 1152, 512), (65, 256, 512), (256, 4096, 256), (129, 640, 4096)])
+def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
+    """Short, narrow layers at 65-256 tokens take the decode family by
+    default (64-row tiles paired 8 workgroup ids apart), including fewer
+    groups than waves."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
 def test_decode_row_tiles_need_whole_rounds(monkeypatch):
     """Row tiles pair workgroups 8 ids apart, which needs the column tiles in
     whole rounds of 8: otherwise the configuration is refused."""

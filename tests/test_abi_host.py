@@ -66,6 +66,11 @@ def test_variant_sizes_and_validation(monkeypatch):
     assert L.qoq_w4a16_gemm(P + 2, 4, 4096, P, 4096, P, None) == ALIGN
     assert L.qoq_w4a16_gemm(P, 0, 4096, P, 4096, P, None) == OK
     assert L.qoq_w4a16_gemm(P, 1 << 20, 1024, P, 4096, P, None) == SHAPE   # 2 M K = 2^31
+    # the comparison kernels address with 32-bit buffer offsets: weights of
+    # 2^31 bytes or more are refused before any launch
+    assert L.qoq_w8a8_gemm(P, P, 4, 1 << 16, P, P, 1 << 15, P, None, None) == SHAPE   # N K = 2^31
+    assert L.qoq_w4a4_gemm(P, 4, 1 << 17, P, 1 << 15, P, None) == SHAPE             # N K / 2 = 2^31
+    assert L.qoq_w4a16_gemm(P, 4, 1 << 17, P, 1 << 15, P, None) == SHAPE
     monkeypatch.setenv("QOQ_VARIANT_CONFIG", "9,9,9,9,9")
     assert L.qoq_w8a8_gemm(P, P, 4, 4096, P, P, 4096, P, None, None) == 8
     assert L.qoq_w4a4_gemm(P, 4, 4096, P, 4096, P, None) == 8

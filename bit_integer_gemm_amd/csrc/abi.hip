@@ -280,6 +280,13 @@ qoq_status check_kv4_heads(int64_t B, int64_t H, int64_t Hkv, int64_t D) {
     return QOQ_OK;
 }
 
+// A dispatch counts its work-items in 32 bits: the attention grid, and the
+// merge of split contexts (64 work-items per (sequence, query head)).
+bool kv_launch_fits(const qoq::Kv4Plan& p, int64_t B, int64_t H) {
+    const int64_t lim = int64_t(1) << 32;
+    return p.grid < lim / (64 * p.waves) && B * H < lim / 64;
+}
+
 // caches of B x H_kv regions of C tokens (512 bytes per token at most) must
 // have byte offsets far inside int64
 bool kv_cache_fits(int64_t B, int64_t Hkv, int64_t C) {
@@ -332,6 +339,7 @@ size_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int
         return 0;
     if (B == 0) return 0;
     const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
+    if (!kv_launch_fits(p, B, H)) return 0;   // the call itself refuses these
     return size_t(qoq::kv4_workspace_bytes(p, B, H));
 }
 
@@ -352,7 +360,7 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
     if (misaligned(q) || misaligned(lambda) || misaligned(cache) || misaligned(out))
         return QOQ_ERR_ALIGN;
     const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
-    if (p.grid > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    if (!kv_launch_fits(p, B, H)) return QOQ_ERR_SHAPE;
     const int64_t need = qoq::kv4_workspace_bytes(p, B, H);
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < size_t(need)) return QOQ_ERR_WORKSPACE;
@@ -403,7 +411,7 @@ qoq_status qoq_kv16_decode_attention(const uint16_t* q, int64_t B, int64_t H, in
     if (q == nullptr || cache == nullptr || lens == nullptr || out == nullptr) return QOQ_ERR_NULL;
     if (misaligned(q) || misaligned(cache) || misaligned(out)) return QOQ_ERR_ALIGN;
     const qoq::Kv4Plan p = qoq::plan_kv4(B, H_kv, max_len);
-    if (p.grid > (int64_t(1) << 31)) return QOQ_ERR_SHAPE;
+    if (!kv_launch_fits(p, B, H)) return QOQ_ERR_SHAPE;
     const int64_t need = qoq::kv4_workspace_bytes(p, B, H);
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < size_t(need)) return QOQ_ERR_WORKSPACE;

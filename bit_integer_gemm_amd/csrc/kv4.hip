@@ -714,7 +714,7 @@ Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (nb + 3) / 4));
     if (const char* env = std::getenv("QOQ_KV4_SPLITS")) {
         const int v = std::atoi(env);
-        if (v > 0) splits = v;
+        if (v > 0) splits = std::min(v, 1 << 16);
     }
     p.splits = int(splits);
     p.bps = int(std::max<int64_t>(1, (nb + splits - 1) / splits));

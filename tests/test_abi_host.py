@@ -106,6 +106,16 @@ def test_kv4_sizes_and_validation(monkeypatch):
     assert att(P + 2, 2, 32, 8, 128, P, P, 64, P, 64, P, None, 0, None) == ALIGN
     assert att(P, 4, 32, 8, 128, P, P, 16384, P, 16384, P, None, 0, None) == WORKSPACE
     assert att(P, 4, 32, 8, 128, P, P, 16384, P, 16384, P, P, 1024, None) == WORKSPACE
+    # a dispatch counts its work-items in 32 bits: 2^20 sequences x 64 query
+    # heads (64 work-items each in the merge, 2^32 in all) are refused, and
+    # have no workspace size
+    assert att(P, 1 << 20, 64, 64, 128, P, P, 32, P, 32, P, None, 0, None) == SHAPE
+    assert L.qoq_kv16_decode_attention(P, 1 << 20, 64, 64, 128, P, 32, P, 32, P, None, 0,
+                                       None) == SHAPE
+    assert L.qoq_kv4_attention_workspace_bytes(1 << 20, 64, 64, 128, 32) == 0
+    monkeypatch.setenv("QOQ_KV4_SPLITS", "1000000000")   # clamped to 2^16 splits
+    assert att(P, 64, 32, 8, 128, P, P, 1 << 20, P, 1 << 20, P, None, 0, None) == SHAPE
+    monkeypatch.delenv("QOQ_KV4_SPLITS")
     app = L.qoq_kv4_append
     assert app(P, P, 2, 0, 8, 128, P, P, P, 64, None) == OK
     assert app(P, P, 2, 5, 8, 128, P, None, P, 64, None) == NULL

@@ -206,6 +206,23 @@ def test_many_splits_merge(monkeypatch):
     _run(2, 8, 2, [600, 100], 640, seed=19, monkeypatch=monkeypatch, splits=32)
 
 
+@pytest.mark.parametrize("B,H,Hkv,lens,C,splits", [
+    # one long context among empty and short ones: most splits of the short
+    # contexts hold no block, an empty context's merge reads none
+    (5, 8, 2, [2000, 0, 33, 1, 700], 2016, 4),
+    (3, 16, 4, [1500, 20, 900], 1504, 12),
+    # every context empty or one token
+    (4, 8, 1, [0, 1, 0, 1], 32, 3),
+    # more contexts than a wave has lanes
+    (100, 4, 1, [int(x) for x in np.random.default_rng(5).integers(0, 200, 100)], 224, 3),
+])
+def test_splits_of_ragged_contexts(B, H, Hkv, lens, C, splits, monkeypatch):
+    """Contexts of very different lengths cut into the same number of
+    splits, sized by the longest: splits past a context's end write nothing
+    and the merge reads only those that hold tokens."""
+    _run(B, H, Hkv, lens, C, seed=37, monkeypatch=monkeypatch, splits=splits)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
 def test_attention_every_split(splits, monkeypatch):
     _run(3, 8, 2, [300, 45, 257], 320, seed=17, monkeypatch=monkeypatch, splits=splits)
@@ -338,6 +355,10 @@ def test_fp16_paired_schedule(paired, monkeypatch):
 @pytest.mark.parametrize("splits", [2, 5])
 def test_fp16_attention_splits(splits, monkeypatch):
     _run16(3, 8, 2, [300, 45, 257], 320, seed=43, monkeypatch=monkeypatch, splits=splits)
+
+
+def test_fp16_splits_of_ragged_contexts(monkeypatch):
+    _run16(5, 8, 2, [2000, 0, 33, 1, 700], 2016, seed=47, monkeypatch=monkeypatch, splits=4)
 
 
 def test_fp16_single_token_is_exact(monkeypatch):

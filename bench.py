@@ -270,15 +270,18 @@ def main():
         for lin in phases[j % n_phase]:
             lin()
 
-    # capture the step into HIP graphs of G consecutive steps (G divides both
-    # the step count and the number of weight-copy phases), on torch's
-    # capture stream; replaying K/G graphs times exactly K steps
-    G = math.gcd(args.steps, n_phase)
+    # capture the steps into HIP graphs on torch's capture stream: one graph
+    # of all K timed steps when K <= 64 (each replay of a graph costs about
+    # 2 us of its own, which a model's decode step, hundreds of kernels in one
+    # graph, spreads much thinner than a 6-kernel step could), else graphs of
+    # G = gcd(K, phases) consecutive steps; replaying K/G graphs times exactly
+    # K steps, and the untimed warm-up rounds up to whole graphs
+    G = args.steps if args.steps <= 64 else math.gcd(args.steps, n_phase)
     for j in range(n_phase):
         eager_step(j)
     torch.cuda.synchronize()
     graphs = []
-    for g0 in range(0, n_phase, G):
+    for g0 in range(0, n_phase if G < args.steps else 1, G):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for j in range(g0, g0 + G):

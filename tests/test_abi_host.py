@@ -357,3 +357,19 @@ def test_unknown_kernel_override_is_rejected_before_launch(monkeypatch):
         monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
         assert f(P, P, 4, 4096, P, P, 4096, 128, P, None, None, 0, None) == 8
         assert qoq.qoq_gemm_workspace_bytes(4, 4096, 4096) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU: --gpus above 1 (or a multi-rank
+    launch) exits with status 2 and a message, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, WORLD_SIZE="1")
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, env=env, timeout=60)
+    assert r.returncode == 2 and "exactly one GPU" in r.stderr and r.stdout == ""
+    env["WORLD_SIZE"] = "4"
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")],
+                       capture_output=True, text=True, env=env, timeout=60)
+    assert r.returncode == 2 and "exactly one GPU" in r.stderr

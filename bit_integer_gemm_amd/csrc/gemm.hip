@@ -1169,8 +1169,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     } else if (M > 64 && M <= 256 && nbt <= 256 && ng <= 32 && nbt % 16 == 0) {
         // short, narrow layers at a few hundred tokens (Llama-3-8B o at
         // M = 256): the decode family's K-split waves over 64-row tiles beat
-        // the 32x32 tiles, which leave half the CUs with one wave per SIMD
-        p.kind = 1; p.mt = 4; p.cb = 2; p.kw = 4; p.pd = 2;
+        // the 32x32 tiles, which leave half the CUs with one wave per SIMD;
+        // 64 channels per workgroup once that still gives 256 workgroups
+        // (o at M = 256: 14.3 -> 13.1 us against 32 channels)
+        p.kind = 1; p.mt = 4; p.cb = nbt >= 256 ? 4 : 2; p.kw = 4; p.pd = 2;
     } else if (M <= 64) {
         p.kind = 2;
         p.cb = 1;
@@ -1195,6 +1197,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         }
         else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
         else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
+        else if (M <= 256 && t42 >= 192) {
+            // a few hundred tokens on a wide layer: 128 x 256 tiles, 8 waves,
+            // one per CU for most CUs -- the 128-row tile dequantizes each
+            // weight for twice the tokens of the 64-row one (Llama-3-8B
+            // gate_up at M = 256: 38.9 -> 36.0 us)
+            p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8;
+        }
         else if (t22 >= 384) { p.mt = 2; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }   // 64 x 256, 8 waves
         else if (((M + 63) / 64) * ((nbt + 7) / 8) < 160 && ng < 64) {
             p.mt = 1; p.cb = 1; p.pd = 4; p.pa = 3;   // 32 x 128 tiles: twice the workgroups

@@ -111,6 +111,22 @@ def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
     assert err.max() <= 2e-3
 
 
+@pytest.mark.parametrize("M,K,N", [(200, 256, 24576), (256, 384, 28672)])
+def test_wide_layer_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
+    """Wide layers at up to 256 tokens with at least 192 tiles of 128 x 256
+    take those tiles with 8 waves by default (the last row tile ragged for
+    M = 200)."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
 def test_decode_row_tiles_need_whole_rounds(monkeypatch):
     """Row tiles pair workgroups 8 ids apart, which needs the column tiles in
     whole rounds of 8: otherwise the configuration is refused."""

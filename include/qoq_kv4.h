@@ -76,7 +76,9 @@ size_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int
  * [H_kv, D], cache as above, lens device int32 [B] (context lengths; values
  * are clamped to [0, min(max_len, capacity)]), max_len host-side bound of
  * the lengths (sets how contexts are split), out [B, H, D] fp16.
- * H % H_kv == 0 and H / H_kv <= 16. QOQ_KV4_SPLITS=<n> forces n splits.
+ * H % H_kv == 0 and H / H_kv <= 16. QOQ_KV4_SPLITS=<n> forces n splits
+ * (at most 65536). QOQ_ERR_SHAPE also when a launch would count 2^32
+ * work-items or more (B * H >= 2^26, or a forced split count that large).
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN, QOQ_ERR_WORKSPACE,
  * QOQ_ERR_HIP. */
 qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int64_t H_kv,

@@ -1197,11 +1197,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         }
         else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
         else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
-        else if (M <= 256 && t42 >= 192) {
-            // a few hundred tokens on a wide layer: 128 x 256 tiles, 8 waves,
-            // one per CU for most CUs -- the 128-row tile dequantizes each
-            // weight for twice the tokens of the 64-row one (Llama-3-8B
-            // gate_up at M = 256: 38.9 -> 36.0 us)
+        else if (M > 128 && M <= 256 && t42 >= 192) {
+            // 129-256 tokens on a wide layer: two rows of 128 x 256 tiles,
+            // 8 waves, one per CU for most CUs -- the 128-row tile
+            // dequantizes each weight for twice the tokens of the 64-row one
+            // (Llama-3-8B gate_up at M = 256: 38.9 -> 36.0 us); below 129
+            // tokens it would leave rows of the tile idle
             p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8;
         }
         else if (t22 >= 384) { p.mt = 2; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }   // 64 x 256, 8 waves

@@ -113,7 +113,7 @@ def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
 
 @pytest.mark.parametrize("M,K,N", [(200, 256, 24576), (256, 384, 28672)])
 def test_wide_layer_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
-    """Wide layers at up to 256 tokens with at least 192 tiles of 128 x 256
+    """Wide layers at 129-256 tokens with at least 192 tiles of 128 x 256
     take those tiles with 8 waves by default (the last row tile ragged for
     M = 200)."""
     monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)

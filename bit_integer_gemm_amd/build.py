@@ -6,6 +6,11 @@ Flags: gfx950 only; -O3; no fast-math; no floating-point contraction (the
 quantizers' fp32 products and divisions must round exactly like IEEE single
 operations); correctly rounded fp32 division; packed-fp32 instructions
 disabled in device code.
+
+Each source is compiled to an object of its own (in parallel, under
+`_build/`), then the objects are linked into the shared library; no kernel
+calls a device function of another source, so no relocatable device code is
+needed.
 """
 from __future__ import annotations
 
@@ -13,12 +18,14 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqoq.so")
+OBJDIR = os.path.join(ROOT, "_build", "obj")
 SOURCES = ["abi.hip", "pack.hip", "act_quant.hip", "gemm.hip", "variants.hip", "kv4.hip",
            "measure.hip"]
 
@@ -27,7 +34,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
@@ -44,16 +50,35 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    objs, cmds = [], []
+    for s in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o")
+        objs.append(obj)
+        cmds.append([cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+                     os.path.join(CSRC, s), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    failed = [r for r in results if r.returncode != 0]
+    for r in results:
+        if r.returncode != 0 or (verbose and r.stderr.strip()):
+            sys.stderr.write(r.stdout + r.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed compiling libqoq sources")
+    tmp = LIB + ".tmp"
+    res = _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libqoq.so")
+        raise RuntimeError("hipcc failed linking libqoq.so")
     os.replace(tmp, LIB)
     return LIB
 

@@ -28,7 +28,8 @@ import torch
 __all__ = [
     "LIB_PATH", "QoQError", "lib", "GROUP", "PACK_FROM_CANONICAL",
     "qoq_packed_weight_bytes", "qoq_act_bytes", "qoq_gemm_workspace_bytes", "qoq_pack_weights",
-    "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_status_string", "qoq_w4a8_linear",
+    "qoq_quantize_act", "qoq_w4a8_gemm", "qoq_w4a8_gemm_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "qoq_status_string", "qoq_w4a8_linear",
     "qoq_linear_workspace_bytes", "qoq_linear_path",
     "PackedWeight", "pack_weights", "pack_canonical", "quantize_act", "w4a8_gemm",
     "Workspace", "empty_act", "w4a8_linear",
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.qoq_quantize_act.restype = ctypes.c_int
         L.qoq_w4a8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.qoq_w4a8_gemm.restype = ctypes.c_int
+        L.qoq_w4a8_gemm_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, i64, i32, vp, vp, vp]
+        L.qoq_w4a8_gemm_noalloc.restype = ctypes.c_int
         L.qoq_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.qoq_linear_workspace_bytes.restype = sz
         L.qoq_w4a8_linear.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp]
@@ -182,6 +185,16 @@ def qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
                   workspace_bytes, stream) -> int:
     return lib().qoq_w4a8_gemm(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, workspace,
                                workspace_bytes, stream)
+
+
+def qoq_w4a8_gemm_noalloc(x8, s_x, M, K, packed, s1, N, group, y, acc_debug, stream) -> int:
+    """qoq_w4a8_gemm with the library's fixed per-GPU scratch array in place
+    of a workspace (nothing allocated; see include/qoq.h)."""
+    return lib().qoq_w4a8_gemm_noalloc(x8, s_x, M, K, packed, s1, N, group, y, acc_debug,
+                                       stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # QOQ_NOALLOC_SCRATCH_BYTES
 
 
 def qoq_linear_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -309,16 +322,27 @@ def quantize_act(x: torch.Tensor, out=None):
 
 
 class Workspace:
-    """A device buffer, grown on demand, for the workspace
-    arguments of qoq_w4a8_gemm and qoq_w4a8_linear. One buffer serves any
-    number of sequential calls on one stream."""
+    """A device buffer, grown on demand, for the workspace arguments of
+    qoq_w4a8_gemm, qoq_w4a8_linear and the attention calls. One buffer
+    serves any number of sequential calls on one stream; calls that may
+    overlap (other streams) need a Workspace each.
+
+    Growing never frees the buffer it replaces: the superseded buffers stay
+    referenced (``retired``) for the Workspace's lifetime, so a HIP graph
+    captured with an earlier, smaller buffer still writes into live memory
+    when it is replayed after a later call has grown the workspace. Code
+    that captures graphs should still pass a Workspace of its own, sized
+    before the capture."""
 
     def __init__(self, device):
         self.device = torch.device(device)
         self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+        self.retired = []
 
     def get(self, nbytes: int) -> torch.Tensor:
         if nbytes > self.buf.numel():
+            if self.buf.numel():
+                self.retired.append(self.buf)
             self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8,
                                    device=self.device)
         return self.buf
@@ -328,9 +352,12 @@ _WORKSPACES = {}
 
 
 def _default_workspace(device: torch.device) -> Workspace:
-    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    """The default Workspace of (device, current stream): calls on different
+    streams never share one."""
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
     if key not in _WORKSPACES:
-        _WORKSPACES[key] = Workspace(torch.device("cuda", key[1]))
+        _WORKSPACES[key] = Workspace(torch.device("cuda", index))
     return _WORKSPACES[key]
 
 

@@ -106,6 +106,28 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
     return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
+qoq_status qoq_w4a8_gemm_noalloc(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
+                                 const void* packed, const uint16_t* s1, int64_t N,
+                                 int32_t group, uint16_t* y, int32_t* acc_debug, void* stream) {
+    static_assert(QOQ_NOALLOC_SCRATCH_BYTES == qoq::kStaticScratchBytes, "scratch size");
+    const qoq_status st = check_weight_shape(N, K, group);
+    if (st != QOQ_OK) return st;
+    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (x8 == nullptr || s_x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr)
+        return QOQ_ERR_NULL;
+    if (misaligned(x8) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
+    const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);
+    if (plan.kind < 0) return QOQ_ERR_CONFIG;
+    if (plan.ws_bytes > qoq::kStaticScratchBytes) return QOQ_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void* scratch = nullptr;
+    if (plan.ws_bytes > 0 && qoq::static_scratch(s, &scratch) != hipSuccess) return QOQ_ERR_HIP;
+    const hipError_t e = qoq::launch_gemm(plan, x8, s_x, M, K, static_cast<const uint8_t*>(packed),
+                                          s1, N, y, acc_debug, scratch, s);
+    return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
 size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
     const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);

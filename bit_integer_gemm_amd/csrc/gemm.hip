@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1395,6 +1396,52 @@ hipError_t launch_linear_fused(const LinearPlan& p, const uint16_t* x, int64_t M
         case 4: return launch_fused_vt<8, 4>(p, x, m, k, packed, rec, ng8, s1, n, y, acc_debug, stream);
         default: return hipErrorInvalidConfiguration;
     }
+}
+
+}  // namespace qoq
+
+// Scratch memory of the allocation-free GEMM entry point: a fixed device
+// array of this library (one copy per GPU, held until the process ends)
+// that stands in for the caller's workspace. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_addr.
+static __device__ __align__(256) uint8_t scratch[qoq::kStaticScratchBytes];
+
+namespace qoq {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void** out) {
+    *out = nullptr;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_addr[dev] == nullptr) {
+        // the lookup runs with the stream's device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace qoq

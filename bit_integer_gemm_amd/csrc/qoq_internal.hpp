@@ -137,6 +137,12 @@ struct LinearPlan {
 
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K);
 
+// Allocation-free GEMM: the library's own scratch array stands in for the
+// workspace. static_scratch returns its device address on the stream's
+// device (looked up on first use per device, then cached).
+constexpr int64_t kStaticScratchBytes = int64_t(64) << 20;
+hipError_t static_scratch(hipStream_t stream, void** out);
+
 // Comparison GEMMs (W8A8 per-channel, W4A4 per-group with partial-sum
 // scaling) on the 32x32 tile skeleton.
 constexpr int kVariantW8A8 = 1;

@@ -175,6 +175,32 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
                          uint16_t* y, int32_t* acc_debug,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the scratch array behind qoq_w4a8_gemm_noalloc (one per GPU). */
+#define QOQ_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/* qoq_w4a8_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, kernels and
+ * results as qoq_w4a8_gemm, bit for bit; where that call would use the
+ * workspace (K split over workgroups), this one uses a fixed scratch array
+ * of QOQ_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held
+ * until the process ends. Its address is looked up on the first call on a
+ * device (the stream's device, or the current device for the null stream);
+ * nothing is ever allocated or freed by this call. Shapes whose workspace
+ * (qoq_gemm_workspace_bytes) exceeds QOQ_NOALLOC_SCRATCH_BYTES are refused
+ * with QOQ_ERR_WORKSPACE before anything is launched. Every call on one GPU
+ * shares that GPU's array and leaves its partial sums there: calls that
+ * overlap in time on one GPU (two streams, two threads) race and give
+ * unspecified results; calls in one stream are ordered and safe. Every
+ * element of the scratch is written before it is read, so nothing needs
+ * clearing between calls.
+ * Errors: as qoq_w4a8_gemm (QOQ_ERR_WORKSPACE for a too large split;
+ * QOQ_ERR_HIP also when the scratch address cannot be looked up). */
+qoq_status qoq_w4a8_gemm_noalloc(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
+                                 const void* packed, const uint16_t* s1, int64_t N,
+                                 int32_t group, uint16_t* y, int32_t* acc_debug,
+                                 void* stream);
+
 /* Workspace bytes qoq_w4a8_linear needs for this shape: 0 when it runs as
  * one fused launch (M <= 8 and K <= 8192), otherwise room for the x8 codes,
  * the token scales and the GEMM's own workspace. No zero-fill is needed.

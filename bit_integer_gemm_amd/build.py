@@ -26,8 +26,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqoq.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
-SOURCES = ["abi.hip", "pack.hip", "act_quant.hip", "gemm.hip", "variants.hip", "kv4.hip",
-           "measure.hip"]
+SOURCES = ["abi.hip", "pack.hip", "act_quant.hip", "gemm.hip", "gemm_ksplit.hip", "gemm_wide.hip", "gemm_stream.hip", "variants.hip",
+           "kv4.hip", "measure.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -56,16 +56,29 @@ def _run(cmd, verbose):
     return subprocess.run(cmd, capture_output=True, text=True)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def _stale(obj: str, src: str) -> bool:
+    """An object older than its source or than any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+                    if f.endswith((".h", ".hpp"))]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, jobs: int | None = None, force: bool = True) -> str:
+    """Compile and link libqoq.so. force=False recompiles only the objects
+    older than their source or a header (for quick rebuilds while editing)."""
     os.makedirs(OBJDIR, exist_ok=True)
     cc = hipcc()
     objs, cmds = [], []
     for s in SOURCES:
         obj = os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o")
+        src = os.path.join(CSRC, s)
         objs.append(obj)
-        cmds.append([cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
-                     os.path.join(CSRC, s), "-o", obj])
-    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)))
+        if force or _stale(obj, src):
+            cmds.append([cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
+    jobs = jobs or min(max(1, len(cmds)), max(1, (os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda c: _run(c, verbose), cmds))
     failed = [r for r in results if r.returncode != 0]
@@ -75,7 +88,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if failed:
         raise RuntimeError("hipcc failed compiling libqoq sources")
     tmp = LIB + ".tmp"
-    res = _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    res = _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp],
+               verbose)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed linking libqoq.so")
@@ -84,4 +98,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, force="--changed" not in sys.argv))

@@ -1005,18 +1005,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-struct Args {
-    const int8_t* x8;
-    const float* s_x;
-    int M, K;
-    const uint8_t* nib;
-    const uint8_t* rec;
-    int ng8;
-    const uint16_t* s1;
-    int N;
-    uint16_t* y;
-    int32_t* acc_debug;
-};
+using Args = GemmArgs;
 
 // Second pass of a split-K launch: partial sums [splits][M][N] -> y.
 hipError_t launch_splitk_epilogue(const GemmPlan& p, const Args& a, const int32_t* part,
@@ -1129,11 +1118,14 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
 //                        LDS, waves side by side along N (K split in two for
 //                        32 < M <= 64, N < 32768 and K >= 8192);
-//   64 < M <= 256, N <= 4096, K <= 4096: decode family, 64-row tiles;
-//   M  > 64:             32x32 tile family: 128 x 512 tiles of 8 waves when
-//                        they fill whole rounds of the CUs, 128 x 256 tiles of
-//                        8 waves for short, deep shapes (N <= 8192; 128 x 512
-//                        with K in two ranges when K >= 16384), else tiles
+//   128 < M <= 256, N <= 8192: K-split 32x32 family (64-row tiles, K split
+//                        over the 4 waves of a workgroup);
+//   64 < M <= 128, N <= 4096, K <= 4096: decode family, 64-row tiles;
+//   M  > 64:             wide-tile family (256 x 256 tiles of 8 waves) when
+//                        they fill whole rounds of the CUs, or for deep,
+//                        narrow shapes (N <= 8192, K >= 16384: K in two
+//                        ranges); otherwise the 32x32 tile family: 128 x 256
+//                        tiles of 8 waves for short, narrow shapes, else tiles
 //                        sized so that ~2 workgroups per CU exist (down to
 //                        32 x 128 for few, short tiles), with K split when
 //                        fewer tiles than CUs remain.
@@ -1167,6 +1159,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         else { p.cb = 1; p.kw = 8; p.pd = 4; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
+    } else if (M > 128 && M <= 256 && nbt <= 512) {
+        // narrow layers at 129-256 tokens (Llama-3-8B qkv / o / down at
+        // M = 256): K-split 32x32 family, 64-row tiles of 64 or 96 columns
+        // (whichever is closer to one workgroup per CU), 4 waves splitting
+        // K, rings of 3 groups (o 12.8 -> 10.5 us, qkv 16.9 -> 13.2 us,
+        // down 32.0 -> 26.5 us against the previous rules)
+        p.kind = 5; p.mt = 2; p.kw = 4; p.pd = 3;
+        const int64_t rows = (M + 63) / 64;
+        p.cb = rows * ((nbt + 3) / 4) > 256 && rows * ((nbt + 5) / 6) >= 192 ? 3 : 2;
     } else if (M > 64 && M <= 256 && nbt <= 256 && ng <= 32 && nbt % 16 == 0) {
         // short, narrow layers at a few hundred tokens (Llama-3-8B o at
         // M = 256): the decode family's K-split waves over 64-row tiles beat
@@ -1188,13 +1189,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         const int64_t rows128 = (M + 127) / 128;
         const int64_t t42 = rows128 * ((nbt + 15) / 16);       // 128 x 256 tiles
         const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
-        const int64_t t_wide = rows128 * ((nbt + 31) / 32);    // 128 x 512 tiles, 8 waves
-        // whole rounds of one wide tile per CU: the tail round is >= 90 % full
-        const bool wide_fills = t_wide >= 512 && (t_wide % 256 == 0 || t_wide % 256 >= 230);
-        if (wide_fills) { p.mt = 4; p.cb = 2; p.pd = 2; p.pa = 1; p.nw = 8; }
+        // whole rounds of one 256 x 256 tile per CU: the tail round is >= 90 % full
+        const int64_t t256 = ((M + 255) / 256) * ((nbt + 15) / 16);
+        const bool wide_fills = t256 >= 512 && (t256 % 256 == 0 || t256 % 256 >= 230);
+        if (wide_fills) {
+            // wide-tile family: 256 x 256 tiles of 8 waves, activations
+            // staged by direct LDS loads three groups deep (Qwen1.5-72B
+            // gate+up at M = 1024: 344-359 -> 330-347 us against 128 x 512
+            // tiles of the 32x32 family)
+            p.kind = 6; p.mt = 8; p.cb = 1; p.nw = 8; p.pd = 3; p.pa = 1;
+        }
         else if (M >= 512 && N <= 8192 && t42 >= 256 && ng >= 128) {
-            // deep and narrow: 128 x 512 tiles, K in two ranges
-            p.mt = 4; p.cb = 2; p.pd = 2; p.pa = 1; p.nw = 8; p.splits = 2;
+            // deep and narrow: wide-tile family, 256 x 256 tiles, K in two
+            // ranges (Qwen1.5-72B down at M = 1024: 192-197 -> 182 us)
+            p.kind = 6; p.mt = 8; p.cb = 1; p.nw = 8; p.pd = 3; p.pa = 1; p.splits = 2;
         }
         else if (M >= 512 && N <= 8192 && t42 >= 256) { p.mt = 4; p.cb = 1; p.pd = 2; p.pa = 1; p.nw = 8; }
         else if (t42 >= 512) { p.mt = 4; p.cb = 2; p.pd = 2; }
@@ -1235,6 +1243,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
                        tile32_config_exists(a, b, c, d, e) && sp >= 1 && sp <= 64) {
                 p.kind = 4; p.mt = a; p.cb = b; p.pd = c; p.pa = d; p.nw = e;
                 p.splits = nf == 7 ? sp : 1;
+            } else if (f == "stream" && (nf == 6 || nf == 7) && small_offsets &&
+                       stream_config_exists(a, b, c, d, e) && sp >= 1 && sp <= 64) {
+                p.kind = 7; p.mt = a; p.cb = b; p.nw = c; p.pd = d; p.pa = e;
+                p.splits = nf == 7 ? sp : 1;
+            } else if (f == "wide" && (nf == 6 || nf == 7) && small_offsets &&
+                       wide_config_exists(a, b, c, d, e) && sp >= 1 && sp <= 64) {
+                p.kind = 6; p.mt = a; p.cb = b; p.nw = c; p.pd = d; p.pa = e;
+                p.splits = nf == 7 ? sp : 1;
+            } else if (f == "ksplit" && nf == 5 && small_offsets && ksplit32_config_exists(a, b, c, d)) {
+                p.kind = 5; p.mt = a; p.cb = b; p.kw = c; p.pd = d;
             } else if (f == "generic" && nf >= 3 && (a == 1 || a == 2 || a == 4) && b == 2) {
                 p.kind = 0; p.mt = a; p.cb = b;
             }
@@ -1248,7 +1266,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
         if (p.grid_y > 1 && tn % 8 != 0) { p.kind = -1; return p; }
         p.grid_x = int(tn * p.grid_y);
-    } else if (p.kind == 4) {
+    } else if (p.kind == 5) {
+        p.grid_x = int(((M + 32 * p.mt - 1) / (32 * p.mt)) * ((nbt + 2 * p.cb - 1) / (2 * p.cb)));
+        p.grid_y = 1;
+    } else if (p.kind == 7) {
+        p.grid_x = int((nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw));
+        p.grid_y = int((M + 32 * p.mt - 1) / (32 * p.mt));
+    } else if (p.kind == 4 || p.kind == 6) {
         const int64_t tm = (M + 32 * p.mt - 1) / (32 * p.mt);
         const int64_t tn = (nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw);
         p.grid_x = int(tm * tn);
@@ -1260,7 +1284,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.grid_x = int((nbt + 4 * p.cb - 1) / (4 * p.cb));
         p.grid_y = int((M + 16 * p.mt - 1) / (16 * p.mt));
     }
-    if (p.kind == 2 || p.kind == 4) {
+    if (p.kind == 2 || p.kind == 4 || p.kind == 6 || p.kind == 7) {
         // split K into whole record chunks of 8 groups; the partial sums
         // [splits][M][N] live in the workspace
         const int64_t want = std::max(1, p.splits);
@@ -1284,6 +1308,15 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
         QOQ_DECODE_CONFIGS(X)
 #undef X
         return hipErrorInvalidConfiguration;
+    }
+    if (p.kind == 5) return launch_ksplit32(p, a, stream);
+    if (p.kind == 6 || p.kind == 7) {
+        int32_t* part = p.splits > 1 ? static_cast<int32_t*>(ws) : nullptr;
+        if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+        const hipError_t e = p.kind == 6 ? launch_wide(p, a, part, stream)
+                                         : launch_stream(p, a, part, stream);
+        if (e != hipSuccess || p.splits == 1) return e;
+        return launch_splitk_epilogue(p, a, part, stream);
     }
     if (p.kind == 4) {
 #define X(A, B, C, D, E)                                                              \

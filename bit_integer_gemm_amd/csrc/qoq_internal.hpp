@@ -107,7 +107,9 @@ inline PackedLayout packed_layout(int64_t N, int64_t K) {
 // workspace-size query and the launcher).
 struct GemmPlan {
     int kind;           // 0: generic, 1: decode (K split over waves), 2: shared-activation,
-                        // 4: 32x32 tile (large M)
+                        // 4: 32x32 tile (large M), 5: K-split 32x32 (K over waves),
+                        // 6: wide tile (activations to LDS by direct loads),
+                        // 7: weight streaming (activation chunks in LDS)
     int mt;             // 16-row MFMA tiles per wave
     int cb;             // 16-column blocks per wave
     int kw;             // decode: waves splitting K; shared-activation: waves per workgroup
@@ -121,6 +123,35 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+// Kernel arguments shared by the GEMM families (packed buffer split into its
+// nibble and record regions).
+struct GemmArgs {
+    const int8_t* x8;
+    const float* s_x;
+    int M, K;
+    const uint8_t* nib;
+    const uint8_t* rec;
+    int ng8;
+    const uint16_t* s1;
+    int N;
+    uint16_t* y;
+    int32_t* acc_debug;
+};
+
+// K-split 32x32 family (gemm_ksplit.hip): plan kind 5, (mt, cb, kw, pd).
+bool ksplit32_config_exists(int mt, int cb, int kw, int pd);
+hipError_t launch_ksplit32(const GemmPlan& p, const GemmArgs& a, hipStream_t stream);
+
+// Wide-tile family (gemm_wide.hip): plan kind 6, (mt, cb, nw, R = pd ring
+// slots, pa workgroups per CU); `part` = split-K partial sums or null.
+bool wide_config_exists(int mt, int cb, int nw, int r, int minb);
+hipError_t launch_wide(const GemmPlan& p, const GemmArgs& a, int32_t* part, hipStream_t stream);
+
+// Weight-streaming family (gemm_stream.hip): plan kind 7, (mt, cb, nw, pd
+// ring depth, pa = groups per activation chunk); `part` as above.
+bool stream_config_exists(int mt, int cb, int nw, int pd, int ch);
+hipError_t launch_stream(const GemmPlan& p, const GemmArgs& a, int32_t* part, hipStream_t stream);
 
 // Launch plan of the fused entry point (activation quantization + GEMM):
 // either one fused launch (small M) or the quantizer into a workspace

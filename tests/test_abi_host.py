@@ -218,11 +218,11 @@ def test_default_plans_split_long_k(monkeypatch):
     ws = qoq.qoq_gemm_workspace_bytes
     assert ws(64, 8192, 24576) == 4 * 64 * 8192 * 4          # Qwen1.5-72B down, M = 64
     assert ws(64, 24576, 8192) == 2 * 64 * 24576 * 4         # Qwen1.5-72B qkv, M = 64
-    assert ws(256, 4096, 14336) == 4 * 256 * 4096 * 4        # Llama-3-8B down, M = 256
     assert ws(1024, 8192, 24576) == 2 * 1024 * 8192 * 4      # Qwen1.5-72B down, M = 1024
     for M, N, K in [(1, 4096, 4096), (8, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
                     (64, 49152, 8192), (256, 6144, 4096), (256, 4096, 4096), (256, 28672, 4096),
-                    (4096, 14336, 4096), (1024, 49152, 8192), (1024, 24576, 8192), (16, 512, 512)]:
+                    (4096, 14336, 4096), (1024, 49152, 8192), (1024, 24576, 8192), (16, 512, 512),
+                    (256, 4096, 14336)]:
         assert ws(M, N, K) == 0, (M, N, K)
 
 

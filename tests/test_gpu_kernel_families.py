@@ -39,6 +39,15 @@ TILE32 = [(4, 2, 2, 2, 4), (4, 2, 1, 2, 4), (4, 1, 2, 2, 4), (2, 2, 2, 2, 4), (2
           (2, 1, 2, 1, 8), (2, 1, 4, 1, 3), (2, 1, 4, 2, 3), (1, 1, 4, 1, 6), (2, 1, 8, 1, 6),
           (4, 1, 2, 1, 8), (4, 2, 2, 1, 8)]
 GENERIC = [(1, 2), (2, 2), (4, 2)]
+STREAM = [(2, 1, 8, 4, 8), (2, 1, 8, 4, 4), (2, 1, 6, 4, 8), (2, 1, 4, 4, 8), (2, 1, 8, 8, 8),
+          (2, 2, 8, 4, 8), (2, 1, 12, 4, 8), (1, 1, 8, 4, 8), (1, 2, 8, 4, 8), (2, 1, 16, 4, 8),
+          (2, 1, 3, 4, 8), (1, 1, 4, 4, 8), (2, 2, 4, 4, 8), (2, 1, 6, 8, 8)]
+WIDE = [(4, 2, 8, 3, 1), (4, 2, 8, 4, 1), (8, 1, 8, 3, 1), (8, 1, 8, 4, 1), (4, 1, 8, 4, 1),
+        (4, 2, 4, 4, 1), (4, 1, 4, 4, 2), (2, 1, 8, 4, 1), (8, 2, 4, 3, 1), (8, 2, 4, 4, 1)]
+KSPLIT = [(1, 1, 8, 2), (1, 2, 8, 2), (2, 1, 8, 2), (2, 2, 8, 2), (4, 1, 8, 2), (2, 2, 4, 2),
+          (4, 1, 4, 2), (2, 1, 8, 4), (1, 1, 16, 2), (2, 3, 4, 2), (1, 3, 8, 2), (2, 2, 4, 3),
+          (2, 2, 4, 4), (2, 3, 4, 3), (2, 3, 4, 4), (4, 1, 4, 3), (4, 1, 4, 4), (1, 1, 8, 4),
+          (1, 2, 8, 3), (2, 1, 8, 3)]
 
 # (M, K, N): odd group counts, N not a multiple of any tile width
 SHAPES_SMALL_M = [(1, 640, 208), (13, 1152, 400), (37, 384, 48), (64, 2048, 528)]
@@ -95,11 +104,46 @@ def test_decode_family_row_tiles(monkeypatch, cfg):
             _run(monkeypatch, _fmt("decode", cfg), M, 1152, N)
 
 
-@pytest.mark.parametrize("M,K,N", [(200, 1152, 512), (65, 256, 512), (256, 4096, 256), (129, 640, 4096)])
+@pytest.mark.parametrize("M,K,N", [(65, 256, 512), (128, 1152, 4096), (100, 4096, 256)])
 def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
-    """Short, narrow layers at 65-256 tokens take the decode family by
+    """Short, narrow layers at 65-128 tokens take the decode family by
     default (64-row tiles paired 8 workgroup ids apart), including fewer
     groups than waves."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("M,K,N", [(200, 1152, 512), (256, 4096, 256), (129, 640, 4096),
+                                   (256, 640, 6144), (193, 1920, 8192), (256, 384, 2064)])
+def test_ksplit_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
+    """Narrow layers (N <= 8192) at 129-256 tokens take the K-split 32x32
+    family by default: 64-row tiles of 64 columns, or of 96 columns when
+    that is closer to one workgroup per CU (N = 6144, 8192); ragged rows
+    (M = 129, 193, 200), fewer groups than waves (K = 256 / 384), odd
+    column counts (N = 2064: the last 32-column tile half outside)."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 256, 65536)])
+def test_wide_tile_plan_when_tiles_fill_rounds(M, K, N, monkeypatch):
+    """Shapes whose 256 x 256 tiles fill whole rounds of the CUs (here 2 x 256
+    tiles, the second row tile ragged at 44 rows) take the wide-tile family
+    by default."""
     monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
@@ -206,3 +250,41 @@ def test_unknown_configuration_is_an_error(monkeypatch):
         with pytest.raises(qoq.QoQError) as e:
             qoq.w4a8_gemm(x8, s_x, pw)
         assert e.value.status == 8
+
+
+@pytest.mark.parametrize("cfg", KSPLIT, ids=[_fmt("ksplit", c) for c in KSPLIT])
+def test_ksplit32_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_SMALL_M + SHAPES_LARGE_M:
+        _run(monkeypatch, _fmt("ksplit", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg", WIDE, ids=[_fmt("wide", c) for c in WIDE])
+def test_wide_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_LARGE_M + SHAPES_SMALL_M[1:2]:
+        _run(monkeypatch, _fmt("wide", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg,splits", [((4, 2, 8, 4, 1), 2), ((8, 1, 8, 3, 1), 3)],
+                         ids=["wide,4,2,8,4,1/2", "wide,8,1,8,3,1/3"])
+def test_wide_family_split_k(monkeypatch, cfg, splits):
+    """K in whole chunks of 8 groups per workgroup row, partial sums added by
+    the second kernel: 2560 inputs = 20 groups in ranges of 16 + 4 (two
+    splits) or 8 + 8 + 4 (three)."""
+    for (M, K, N) in [(300, 2560, 528), (64, 2560, 1040)]:
+        _run(monkeypatch, _fmt("wide", cfg) + f",{splits}", M, K, N)
+
+
+@pytest.mark.parametrize("cfg", STREAM, ids=[_fmt("stream", c) for c in STREAM])
+def test_stream_family(monkeypatch, cfg):
+    for (M, K, N) in SHAPES_SMALL_M + SHAPES_LARGE_M[:1]:
+        _run(monkeypatch, _fmt("stream", cfg), M, K, N)
+
+
+@pytest.mark.parametrize("cfg,splits", [((2, 1, 8, 4, 8), 2), ((2, 1, 4, 4, 8), 3), ((1, 1, 8, 4, 8), 4)],
+                         ids=["stream,2,1,8,4,8/2", "stream,2,1,4,4,8/3", "stream,1,1,8,4,8/4"])
+def test_stream_family_split_k(monkeypatch, cfg, splits):
+    """K ranges of whole 8-group record chunks per workgroup row (20 groups:
+    16 + 4, 8 + 8 + 4, or 8 + 8 + 4 with an empty fourth range folded away),
+    chunks of activations shorter than CH at the end of a range."""
+    for (M, K, N) in [(64, 2560, 528), (17, 2560, 1040), (100, 2560, 208)]:
+        _run(monkeypatch, _fmt("stream", cfg) + f",{splits}", M, K, N)

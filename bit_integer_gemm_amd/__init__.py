@@ -364,7 +364,8 @@ def _default_workspace(device: torch.device) -> Workspace:
 def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,
               y: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
     """y fp16 [M, N] = fp16(acc * s_x * s1) for x8 / s_x from quantize_act
-    (M = len(s_x)); also returns acc int32 if asked."""
+    (M = len(s_x)); also returns acc int32 if asked (acc_debug=True, or an
+    int32 [M, N] tensor to write the accumulators into)."""
     _need_gpu(s_x, "s_x", torch.float32)
     if s_x.dim() != 1:
         raise ValueError("s_x must be 1-D [M]")
@@ -373,7 +374,15 @@ def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: b
     dev = x8.device
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.float16, device=dev)
-    acc = torch.empty((M, w.N), dtype=torch.int32, device=dev) if acc_debug else None
+    if isinstance(acc_debug, torch.Tensor):
+        _need_gpu(acc_debug, "acc_debug", torch.int32)
+        if tuple(acc_debug.shape) != (M, w.N):
+            raise ValueError(f"acc_debug must have shape ({M}, {w.N})")
+        acc = acc_debug
+    else:
+        acc = torch.empty((M, w.N), dtype=torch.int32, device=dev) if acc_debug else None
+    if tuple(y.shape) != (M, w.N) or y.dtype != torch.float16:
+        raise ValueError(f"y must be float16 of shape ({M}, {w.N})")
     ws_bytes = qoq_gemm_workspace_bytes(M, w.N, K) if M > 0 else 0
     ws_ptr = None
     if ws_bytes:
@@ -383,7 +392,7 @@ def w4a8_gemm(x8: torch.Tensor, s_x: torch.Tensor, w: PackedWeight, acc_debug: b
     _check(qoq_w4a8_gemm(x8.data_ptr(), s_x.data_ptr(), M, K, w.packed.data_ptr(),
                          w.s1.data_ptr(), w.N, w.group, y.data_ptr(), _ptr(acc), ws_ptr,
                          ws_bytes, _stream(dev)), "qoq_w4a8_gemm")
-    return (y, acc) if acc_debug else y
+    return (y, acc) if acc is not None else y
 
 
 def w4a8_linear(x: torch.Tensor, w: PackedWeight, acc_debug: bool = False,

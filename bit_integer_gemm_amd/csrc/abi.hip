@@ -13,6 +13,19 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // Largest K and N the 32-bit index arithmetic of the kernels supports.
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 
+// Largest K (a multiple of 128) whose INT32 accumulators stay exact:
+// |acc| <= K * 127 * 121 < 2^31 (activation codes within 127, dequantized
+// weights within 121 by the protective range).
+constexpr int64_t kMaxAccK = 139648;
+// The same bound for the W8A8 comparison GEMM (weights within 127).
+constexpr int64_t kMaxAccKW8A8 = 133120;
+static_assert(kMaxAccK * 127 * 121 < (int64_t(1) << 31) && (kMaxAccK + 128) * 127 * 121 >= (int64_t(1) << 31),
+              "accumulator bound");
+static_assert(kMaxAccKW8A8 * 127 * 127 < (int64_t(1) << 31) &&
+              (kMaxAccKW8A8 + 128) * 127 * 127 >= (int64_t(1) << 31), "accumulator bound");
+
+qoq_status check_gemm_k(int64_t K) { return K > kMaxAccK ? QOQ_ERR_SHAPE : QOQ_OK; }
+
 qoq_status check_weight_shape(int64_t N, int64_t K, int32_t group) {
     if (group != qoq::kGroup) return QOQ_ERR_GROUP;
     if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return QOQ_ERR_SHAPE;
@@ -35,7 +48,9 @@ size_t qoq_act_bytes(int64_t M, int64_t K) {
 }
 
 size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim ||
+        check_gemm_k(K) != QOQ_OK)
+        return 0;
     const qoq::GemmPlan plan = qoq::plan_gemm(M, N, K);
     return plan.kind < 0 ? 0 : size_t(plan.ws_bytes);
 }
@@ -88,7 +103,7 @@ qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
                          size_t workspace_bytes, void* stream) {
     const qoq_status st = check_weight_shape(N, K, group);
     if (st != QOQ_OK) return st;
-    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M < 0 || M > kMaxDim || check_gemm_k(K) != QOQ_OK) return QOQ_ERR_SHAPE;
     if (M == 0) return QOQ_OK;
     if (x8 == nullptr || s_x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr)
         return QOQ_ERR_NULL;
@@ -112,7 +127,7 @@ qoq_status qoq_w4a8_gemm_noalloc(const int8_t* x8, const float* s_x, int64_t M, 
     static_assert(QOQ_NOALLOC_SCRATCH_BYTES == qoq::kStaticScratchBytes, "scratch size");
     const qoq_status st = check_weight_shape(N, K, group);
     if (st != QOQ_OK) return st;
-    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M < 0 || M > kMaxDim || check_gemm_k(K) != QOQ_OK) return QOQ_ERR_SHAPE;
     if (M == 0) return QOQ_OK;
     if (x8 == nullptr || s_x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr)
         return QOQ_ERR_NULL;
@@ -129,13 +144,17 @@ qoq_status qoq_w4a8_gemm_noalloc(const int8_t* x8, const float* s_x, int64_t M, 
 }
 
 size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return 0;
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim ||
+        check_gemm_k(K) != QOQ_OK)
+        return 0;
     const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);
     return plan.valid ? size_t(plan.ws_bytes) : 0;
 }
 
 int qoq_linear_path(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim) return -1;
+    if (M <= 0 || check_weight_shape(N, K, qoq::kGroup) != QOQ_OK || M > kMaxDim ||
+        check_gemm_k(K) != QOQ_OK)
+        return -1;
     const qoq::LinearPlan plan = qoq::plan_linear(M, N, K);
     if (!plan.valid) return -1;
     return plan.fused ? 1 : 0;
@@ -147,7 +166,7 @@ qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const void* 
                            void* stream) {
     const qoq_status st = check_weight_shape(N, K, group);
     if (st != QOQ_OK) return st;
-    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M < 0 || M > kMaxDim || check_gemm_k(K) != QOQ_OK) return QOQ_ERR_SHAPE;
     if (M == 0) return QOQ_OK;
     if (x == nullptr || packed == nullptr || s1 == nullptr || y == nullptr) return QOQ_ERR_NULL;
     if (misaligned(x) || misaligned(packed) || misaligned(y)) return QOQ_ERR_ALIGN;
@@ -192,7 +211,7 @@ qoq_status qoq_w8a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t 
                          int32_t* acc_debug, void* stream) {
     const qoq_status st = check_weight_shape(N, K, qoq::kGroup);
     if (st != QOQ_OK) return st;
-    if (M < 0 || M > kMaxDim) return QOQ_ERR_SHAPE;
+    if (M < 0 || M > kMaxDim || K > kMaxAccKW8A8) return QOQ_ERR_SHAPE;
     if (M == 0) return QOQ_OK;
     if (x8 == nullptr || s_x == nullptr || packed == nullptr || s == nullptr || y == nullptr)
         return QOQ_ERR_NULL;

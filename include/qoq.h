@@ -61,6 +61,12 @@ typedef enum qoq_status {
 /* Group size of level 2 (inputs of one output channel per group). */
 #define QOQ_GROUP 128
 
+/* Largest K of the GEMM entry points: the INT32 accumulators stay exact
+ * while K * 127 * 121 < 2^31 (activation codes within 127, dequantized
+ * weights within 121); larger K is refused with QOQ_ERR_SHAPE (the packer
+ * accepts any K). */
+#define QOQ_MAX_GEMM_K 139648
+
 /* Version of the packed-weight layout produced by qoq_pack_weights. */
 #define QOQ_PACKED_LAYOUT_VERSION 1
 
@@ -154,7 +160,8 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * avoid); "Part5 LLM部署技术" section 3 (no partial-sum dequantization).
  *   x8, s_x      from qoq_quantize_act: int8 codes in the activation tile
  *                layout (qoq_act_bytes(M, K) bytes), [M] fp32.
- *   M >= 0, K > 0, K % 128 == 0, N > 0, N % 16 == 0, group == 128.
+ *   M >= 0, K > 0, K % 128 == 0, K <= QOQ_MAX_GEMM_K, N > 0, N % 16 == 0,
+ *   group == 128.
  *   packed, s1   from qoq_pack_weights for the same N, K.
  *   y            out [M,N] fp16 bits, row-major: fp16(acc * s_x[m] * s1[n]).
  *   acc_debug    NULL, or out [M,N] int32: the exact accumulators.
@@ -221,7 +228,8 @@ int qoq_linear_path(int64_t M, int64_t N, int64_t K);
  * on fusing the CUDA-core work into the GEMM). Other shapes run the
  * quantizer into `workspace`, then the GEMM.
  *   x            [M,K] fp16 bits, row-major, 16-byte aligned.
- *   M >= 0, K > 0, K % 128 == 0, N > 0, N % 16 == 0, group == 128.
+ *   M >= 0, K > 0, K % 128 == 0, K <= QOQ_MAX_GEMM_K, N > 0, N % 16 == 0,
+ *   group == 128.
  *   packed, s1   from qoq_pack_weights for the same N, K.
  *   y            out [M,N] fp16 bits.   acc_debug  NULL or out [M,N] int32.
  *   workspace    qoq_linear_workspace_bytes(M, N, K) bytes, 16-byte aligned

@@ -58,7 +58,8 @@ qoq_status qoq_w8a8_pack_weights(const float* W, int64_t N, int64_t K, void* pac
 
 /* W8A8 GEMM: x8/s_x from qoq_quantize_act, y out [M,N] fp16, acc_debug NULL
  * or out [M,N] int32 (exact accumulators). Requires N*K and the x8 buffer
- * below 2^31 bytes. Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN,
+ * below 2^31 bytes and K <= 133120 (K * 127 * 127 < 2^31: the INT32
+ * accumulators stay exact). Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN,
  * QOQ_ERR_CONFIG, QOQ_ERR_HIP. */
 qoq_status qoq_w8a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
                          const void* packed, const uint16_t* s, int64_t N, uint16_t* y,

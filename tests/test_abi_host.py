@@ -7,11 +7,12 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qoq.h")
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 OK, NULL, SHAPE, ALIGN, GROUP, WORKSPACE, HIP, FLAGS = range(8)
 P = 0x10000  # a 16-byte aligned address that is never dereferenced
@@ -373,3 +374,33 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py")],
                        capture_output=True, text=True, env=env, timeout=60)
     assert r.returncode == 2 and "exactly one GPU" in r.stderr
+
+
+def test_gemm_refuses_k_beyond_exact_accumulation():
+    """K above 139648 could wrap the INT32 accumulators (K * 127 * 121 >= 2^31
+    from there on): the GEMM entry points refuse it before any launch, the
+    size queries return 0 / -1; W8A8 (weights within 127) stops at 133120."""
+    K_ok, K_bad = 139648, 139648 + 128
+    assert qoq.qoq_gemm_workspace_bytes(64, 4096, K_bad) == 0
+    assert qoq.qoq_linear_workspace_bytes(64, 4096, K_bad) == 0
+    assert qoq.qoq_linear_path(64, 4096, K_bad) == -1
+    assert qoq.qoq_linear_path(64, 4096, K_ok) in (0, 1)
+    assert qoq.qoq_w4a8_gemm(P, P, 8, K_bad, P, P, 4096, 128, P, None, None, 0, None) == SHAPE
+    assert qoq.qoq_w4a8_gemm_noalloc(P, P, 8, K_bad, P, P, 4096, 128, P, None, None) == SHAPE
+    assert qoq.qoq_w4a8_linear(P, 8, K_bad, P, P, 4096, 128, P, None, None, 0, None) == SHAPE
+    assert qoq.lib().qoq_w8a8_gemm(P, P, 8, 133120 + 128, P, P, 4096, P, None, None) == SHAPE
+    assert qoq.qoq_packed_weight_bytes(16, K_bad) > 0   # packing any K is fine
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="needs a host without a visible GPU: the launch must fail, not run")
+def test_launch_failure_reports_hip_error():
+    """With no GPU the host checks pass and the launch itself fails: every
+    entry point returns QOQ_ERR_HIP (nothing runs; the pointers are never
+    dereferenced)."""
+    assert qoq.qoq_quantize_act(P, 4, 128, P, P, None) == HIP
+    assert qoq.qoq_w4a8_gemm(P, P, 4, 128, P, P, 16, 128, P, None, None, 0, None) == HIP
+    assert qoq.qoq_w4a8_linear(P, 4, 128, P, P, 16, 128, P, None, P, 1 << 20, None) == HIP
+    assert qoq.qoq_pack_weights(P, 16, 128, 128, P, P, None, 0, None) == HIP
+    # the allocation-free GEMM fails already when it looks up its scratch array
+    assert qoq.qoq_w4a8_gemm_noalloc(P, P, 64, 16384, P, P, 4096, 128, P, None, None) == HIP

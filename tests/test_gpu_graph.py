@@ -14,7 +14,7 @@ import oracle
 import workloads as wl
 from act_layout import act_rows
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

@@ -13,8 +13,9 @@ import torch
 
 import oracle
 import workloads as wl
+from guard import Guarded, GuardedWorkspace
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,22 +58,38 @@ _cases = {}
 
 
 def _case(M, K, N):
+    """Packed weights, quantized activations (written inside guard bands) and
+    the oracle's result for one seeded shape."""
     key = (M, K, N)
     if key not in _cases:
         W, X, _ = wl.make_inputs(M, K, N, seed=M + 3 * K + 7 * N)
         pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
-        x8, s_x = qoq.quantize_act(torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV))
+        gx8 = Guarded(((M + 15) // 16, K // 16, 16, 16), torch.int8, DEV)
+        gsx = Guarded((M,), torch.float32, DEV)
+        x8, s_x = qoq.quantize_act(torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV),
+                                   out=(gx8.t, gsx.t))
+        gx8.check("x8")
+        gsx.check("s_x")
         ref = oracle.w4a8_linear(X, W)
         _cases[key] = (pw, x8, s_x, ref)
     return _cases[key]
 
 
 def _run(monkeypatch, cfg, M, K, N):
+    """One forced configuration: accumulators bit-exact, y within the
+    tolerance, and nothing written outside y, the accumulators or the
+    workspace (guard bands on all three)."""
     pw, x8, s_x, ref = _case(M, K, N)
     monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
     print(f"\n[gpu-case] {cfg} M={M} K={K} N={N}", flush=True)
-    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    gy = Guarded((M, N), torch.float16, DEV)
+    gacc = Guarded((M, N), torch.int32, DEV)
+    ws = GuardedWorkspace(qoq.qoq_gemm_workspace_bytes(M, N, K), DEV)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=gacc.t, y=gy.t, workspace=ws)
     torch.cuda.synchronize()
+    gy.check("y")
+    gacc.check("acc_debug")
+    ws.check()
     got = acc.cpu().numpy().astype(np.int64)
     assert np.array_equal(got, ref["acc"]), f"{cfg}: acc differs at {np.argwhere(got != ref['acc'])[:4]}"
     yy = y.cpu().numpy().astype(np.float64)

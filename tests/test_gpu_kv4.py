@@ -19,7 +19,7 @@ import oracle
 import workloads as wl
 from kv4_layout import decode_cache
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads as wl
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

@@ -4,7 +4,7 @@ buffer, reaches the sink; an all-zero buffer leaves it untouched."""
 import pytest
 import torch
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

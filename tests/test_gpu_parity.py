@@ -18,8 +18,9 @@ import torch
 import oracle
 import workloads as wl
 from act_layout import act_rows
+from guard import Guarded, GuardedWorkspace
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,13 +34,30 @@ def _announce(*what):
 
 
 def gpu_run(W, X, canonical=True, acc_debug=True):
+    """Pack, quantize and multiply on the GPU with every output (x8, s_x, y,
+    the accumulators, the workspace) inside guard bands that are checked
+    after each launch."""
+    M, K = X.shape
+    N = W.shape[0]
     Wd = torch.from_numpy(W).to(DEV)
     Xd = torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV)
     pw = qoq.pack_weights(Wd, canonical=canonical)
-    x8, s_x = qoq.quantize_act(Xd)
-    out = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=acc_debug)
+    gx8 = Guarded(((M + 15) // 16, K // 16, 16, 16), torch.int8, DEV)
+    gsx = Guarded((M,), torch.float32, DEV)
+    x8, s_x = qoq.quantize_act(Xd, out=(gx8.t, gsx.t))
+    gx8.check("x8")
+    gsx.check("s_x")
+    gy = Guarded((M, N), torch.float16, DEV)
+    gacc = Guarded((M, N), torch.int32, DEV) if acc_debug else None
+    ws = GuardedWorkspace(qoq.qoq_gemm_workspace_bytes(M, N, K), DEV)
+    out = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=gacc.t if acc_debug else False, y=gy.t,
+                        workspace=ws)
     y, acc = out if acc_debug else (out, None)
     torch.cuda.synchronize()
+    gy.check("y")
+    ws.check()
+    if acc_debug:
+        gacc.check("acc_debug")
     return pw, x8, s_x, y, acc
 
 
@@ -229,24 +247,70 @@ def test_empty_batch_is_a_no_op():
     assert x8b.shape == (0, 16, 16, 16) and sxb.shape == (0,)
 
 
-def test_workspace_is_reusable():
-    """Split-K calls leave the workspace zeroed: back-to-back calls of
-    different shapes sharing one workspace give the oracle's results."""
-    ws = qoq.Workspace(DEV)
-    for (M, K, N) in [(8, 4096, 1024), (1, 2048, 512), (8, 4096, 1024), (40, 1024, 256)]:
-        _announce("workspace reuse", M, K, N)
-        W, X, _ = wl.make_inputs(M, K, N, seed=3)
-        Wd = torch.from_numpy(W).to(DEV)
-        pw = qoq.pack_weights(Wd)
+# shapes whose plan keeps split-K partial sums in the workspace: the default
+# plans of the shared-activation and 32x32 families, and forced splits of the
+# shared-activation, wide-tile and weight-streaming families
+SPLIT_CASES = [(64, 16384, 4096, None), (128, 8192, 1024, None),
+               (64, 2560, 528, "lds,4,1,4,2,3"), (300, 2560, 528, "wide,4,2,8,4,1,2"),
+               (40, 2560, 1040, "stream,2,1,8,4,8,3"), (64, 16384, 4096, None)]
+
+
+def test_workspace_is_reusable(monkeypatch):
+    """One workspace (with guard bands) serves split-K calls of different
+    shapes and families back to back: each call writes all of its partial
+    sums before reading them, so stale sums of the previous call never leak
+    into the result, and nothing is written outside the workspace."""
+    need = []
+    for (M, K, N, cfg) in SPLIT_CASES:
+        if cfg:
+            monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+        else:
+            monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+        need.append(qoq.qoq_gemm_workspace_bytes(M, N, K))
+    assert all(b > 0 for b in need), need
+    ws = GuardedWorkspace(max(need), DEV)
+    for (M, K, N, cfg) in SPLIT_CASES:
+        if cfg:
+            monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+        else:
+            monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+        _announce("workspace reuse", M, K, N, cfg)
+        W, X, _ = wl.make_inputs(M, K, N, seed=3 + M + N)
+        pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
         x8, s_x = qoq.quantize_act(torch.from_numpy(X.view(np.uint16)).view(torch.float16).to(DEV))
-        y1, acc1 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True, workspace=ws)
-        y2, acc2 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True, workspace=ws)
-        ref = oracle.w4a8_linear(X, W)
-        assert np.array_equal(acc1.cpu().numpy().astype(np.int64), ref["acc"])
-        assert np.array_equal(acc2.cpu().numpy().astype(np.int64), ref["acc"])
-        assert torch.equal(y1, y2)
-    if ws.buf.numel():
-        assert int(ws.buf.count_nonzero()) == 0
+        y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True, workspace=ws)
+        ws.check()
+        q = oracle.quantize_weights(W)
+        w8 = oracle.dequantize_level2(q["q4"], q["s2"], q["z"], wl.GROUP)
+        x8_ref, sx_ref = oracle.quantize_act(X)
+        acc_ref = oracle.int_gemm_fp64(x8_ref, w8)
+        assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+        check_y(y.cpu().numpy().astype(np.float64), oracle.epilogue(acc_ref, sx_ref, q["s1"]))
+
+
+def test_prefill_full_size_all_outputs(monkeypatch):
+    """The 4096-token prefill workload (M = 4096, K = 4096, N = 14336) in the
+    benchmark's launch configuration, every one of its 58.7 M outputs: the
+    INT32 accumulators bit-exact against the oracle's exact GEMM (fp64 BLAS
+    on the integer codes, exact below 2^53) and y within the tolerance."""
+    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    w = wl.WORKLOADS["prefill"]
+    shape = w.shapes[0]
+    M = w.Ms[0]
+    _announce("prefill all outputs", M, shape.K, shape.N)
+    W, X, _ = wl.make_case(w, shape, M)
+    pw, x8, s_x, y, acc = gpu_run(W, X, canonical=False)
+    q = oracle.quantize_weights(W)
+    w8 = oracle.dequantize_level2(q["q4"], q["s2"], q["z"], wl.GROUP)
+    del W
+    x8_ref, sx_ref = oracle.quantize_act(X)
+    assert np.array_equal(act_rows(x8, M), x8_ref), "x8"
+    acc_ref = oracle.int_gemm_fp64(x8_ref, w8)
+    got = acc.cpu().numpy()
+    bad = np.argwhere(got != acc_ref)
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first at {bad[:4]}"
+    err = check_y(y.cpu().numpy().astype(np.float64), oracle.epilogue(acc_ref, sx_ref, q["s1"]))
+    print(f"[gpu-case] ok, all {M * shape.N} outputs, max rel err {err:.2e}", flush=True)
 
 
 # ---------------------------------------------------------------------------

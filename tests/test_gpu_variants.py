@@ -13,7 +13,7 @@ import workloads as wl
 from act_layout import act_rows
 from variant_layout import w4_codes_scales, w4a16_codes_scales_zeros, w8_codes, x4_codes_scales
 
-qoq = pytest.importorskip("bit_integer_gemm_amd")
+import bit_integer_gemm_amd as qoq  # noqa: E402  (a broken binding must fail, not skip)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

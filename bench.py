@@ -572,7 +572,6 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
     activations), GEMM kernels alone on pre-quantized inputs, each at its
     default launch plan and all four at one common 64 x 128 tile (4 waves, 2
     workgroups per CU) so that only the format differs."""
-    import os as _os
     out = []
     common = "2,1,2,2,4"
     for key, sname, M in VARIANT_SHAPES:
@@ -619,18 +618,18 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
 
         rec = dict(workload=key, shape=sname, M=M, K=K, N=N)
         ops = wl.algorithmic_ops(M, K, N)
-        for label, env_key, env_val, make in (
+        for label, tune_key, tune_val, make in (
                 ("w4a8_qoq", None, None, lambda: q_calls(None)),
                 ("w8a8", None, None, w8_calls),
                 ("w4a4", None, None, w4_calls),
                 ("w4a16", None, None, w16_calls),
-                ("w4a8_qoq_common_tile", "QOQ_GEMM_CONFIG", "tile32," + common, lambda: q_calls(None)),
-                ("w8a8_common_tile", "QOQ_VARIANT_CONFIG", common, w8_calls),
-                ("w4a4_common_tile", "QOQ_VARIANT_CONFIG", common, w4_calls),
-                ("w4a16_common_tile", "QOQ_VARIANT_CONFIG", common, w16_calls)):
-            saved = {k: _os.environ.pop(k, None) for k in ("QOQ_GEMM_CONFIG", "QOQ_VARIANT_CONFIG")}
-            if env_key:
-                _os.environ[env_key] = env_val
+                ("w4a8_qoq_common_tile", "gemm", "tile32," + common, lambda: q_calls(None)),
+                ("w8a8_common_tile", "variant", common, w8_calls),
+                ("w4a4_common_tile", "variant", common, w4_calls),
+                ("w4a16_common_tile", "variant", common, w16_calls)):
+            qoq.clear_tuning()
+            if tune_key:
+                qoq.set_tuning(tune_key, tune_val)
             try:
                 calls = make()
                 for cl in calls[:2]:
@@ -641,10 +640,7 @@ def variant_comparison(torch, qoq, blocker, dev, ws, iters):
                 rec[label + "_us"] = round(t * 1e6, 2)
                 rec[label + "_tops"] = round(ops / t / 1e12, 1)
             finally:
-                for k, v in saved.items():
-                    _os.environ.pop(k, None)
-                    if v is not None:
-                        _os.environ[k] = v
+                qoq.clear_tuning()
         out.append(rec)
         del cq, c8, c4, c16, pw, p8, p4, p16
         torch.cuda.empty_cache()

@@ -37,7 +37,7 @@ __all__ = [
     "w4a16_pack_weights", "w4a16_gemm",
     "kv4_cache_bytes", "kv4_alloc_cache", "kv4_smooth_factors", "kv4_append",
     "kv4_decode_attention", "kv16_alloc_cache", "kv16_append", "kv16_decode_attention",
-    "qoq_stream_read",
+    "qoq_stream_read", "set_tuning", "get_tuning", "clear_tuning", "TUNING_KEYS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqoq.so")
@@ -140,6 +140,8 @@ def lib() -> ctypes.CDLL:
         L.qoq_w4a16_gemm.restype = ctypes.c_int
         L.qoq_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, vp]
         L.qoq_stream_read.restype = ctypes.c_int
+        L.qoq_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
+        L.qoq_set_tuning.restype = ctypes.c_int
         L.qoq_status_string.argtypes = [ctypes.c_int]
         L.qoq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -151,6 +153,33 @@ def lib() -> ctypes.CDLL:
 # ---------------------------------------------------------------------------
 def qoq_status_string(status: int) -> str:
     return lib().qoq_status_string(int(status)).decode()
+
+
+TUNING_KEYS = ("gemm", "variant", "kv4_splits", "kv4_paired")
+_TUNING = {}
+
+
+def set_tuning(key: str, value: Optional[str]) -> None:
+    """Force a launch configuration (qoq_set_tuning; measurements and tests
+    only): key in TUNING_KEYS, value None or "" to clear."""
+    v = None if value in (None, "") else str(value)
+    st = lib().qoq_set_tuning(key.encode(), None if v is None else v.encode())
+    if st != 0:
+        raise QoQError(st, "qoq_set_tuning")
+    if v is None:
+        _TUNING.pop(key, None)
+    else:
+        _TUNING[key] = v
+
+
+def get_tuning(key: str) -> Optional[str]:
+    """The value last set through set_tuning (None when unset)."""
+    return _TUNING.get(key)
+
+
+def clear_tuning() -> None:
+    for k in TUNING_KEYS:
+        set_tuning(k, None)
 
 
 def qoq_stream_read(buf, nbytes: int, workgroups: int, sink, stream) -> int:

@@ -6,7 +6,19 @@
 #include "qoq_kv4.h"
 #include "qoq_internal.hpp"
 
+#include <cstring>
+#include <mutex>
+#include <string>
+
 namespace {
+
+// Plan overrides set by qoq_set_tuning (measurement and test aid; the only
+// mutable state of the library besides the no-alloc entry point's scratch
+// address cache).
+std::mutex tune_mu;
+std::string tune_val[qoq::kTuneCount];
+const char* const tune_key[qoq::kTuneCount] = {"gemm", "variant", "kv4_splits", "kv4_paired"};
+
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -35,7 +47,25 @@ qoq_status check_weight_shape(int64_t N, int64_t K, int32_t group) {
 
 }  // namespace
 
+std::string qoq::tuning(TuningKey key) {
+    std::lock_guard<std::mutex> lock(tune_mu);
+    return tune_val[key];
+}
+
 extern "C" {
+
+qoq_status qoq_set_tuning(const char* key, const char* value) {
+    if (key == nullptr) return QOQ_ERR_NULL;
+    for (int k = 0; k < qoq::kTuneCount; ++k) {
+        if (std::strcmp(key, tune_key[k]) == 0) {
+            std::lock_guard<std::mutex> lock(tune_mu);
+            tune_val[k] = value ? value : "";
+            return QOQ_OK;
+        }
+    }
+    return QOQ_ERR_CONFIG;
+}
+
 
 size_t qoq_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
     if (check_weight_shape(N, K, group) != QOQ_OK) return 0;
@@ -474,7 +504,7 @@ const char* qoq_status_string(int status) {
         case QOQ_ERR_WORKSPACE: return "workspace missing or too small";
         case QOQ_ERR_HIP: return "HIP kernel launch failed";
         case QOQ_ERR_FLAGS: return "unknown flag bits";
-        case QOQ_ERR_CONFIG: return "QOQ_GEMM_CONFIG / QOQ_VARIANT_CONFIG names no compiled kernel configuration for this shape";
+        case QOQ_ERR_CONFIG: return "a tuning override names no compiled kernel configuration for this shape, or an unknown tuning key";
         default: return "unknown status";
     }
 }

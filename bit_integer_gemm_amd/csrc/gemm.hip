@@ -1107,14 +1107,16 @@ bool decode_config_exists(int mt, int cb, int kw, int pd) {
 }  // namespace
 
 // Launch plan (defaults chosen from sweeps on MI355X over the workload
-// shapes; QOQ_GEMM_CONFIG="<family>,<params>" overrides it for A/B runs,
-// host-side only; a value naming no compiled configuration makes the call
-// fail before anything is launched):
+// shapes; the "gemm" tuning key (qoq_set_tuning) "<family>,<params>"
+// overrides it for A/B runs, host-side only; a value naming no compiled
+// configuration makes the call fail before anything is launched):
 //   M <= 64, N <= 8192:  decode family -- K split over the waves of a
 //                        workgroup, one or two column blocks per workgroup;
 //                        for 32 < M <= 64, N >= 4096 and K >= 16384 the
 //                        shared-activation family with K split over
 //                        workgroups instead;
+//   32 < M <= 64, 18432 <= N <= 30720, K >= 4096: K-split 32x32 family,
+//                        64 x 96 tiles;
 //   M <= 64, N  > 8192:  shared-activation family -- activations staged in
 //                        LDS, waves side by side along N (K split in two for
 //                        32 < M <= 64, N < 32768 and K >= 8192);
@@ -1150,6 +1152,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         // over K, about one workgroup of 8 waves per CU
         p.kind = 2; p.cb = 1; p.kw = 8; p.pd = 4;
         p.splits = int(std::min<int64_t>(std::max<int64_t>(256 / ((nbt + 7) / 8), 1), ng / 32));
+    } else if (M > 32 && M <= 64 && nbt >= 1152 && nbt <= 1920 && ng >= 32) {
+        // 33-64 tokens on layers of 18432-30720 columns (Qwen1.5-72B qkv at
+        // M = 64): K-split 32x32 family, 64 x 96 tiles (about one per CU),
+        // 4 waves splitting K, rings of 3 groups (31.3-31.7 -> 27.1 us
+        // against the shared-activation family with K in two ranges)
+        p.kind = 5; p.mt = 2; p.cb = 3; p.kw = 4; p.pd = 3;
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
         if (p.mt == 1) { p.cb = 1; p.kw = 8; p.pd = 4; }
@@ -1225,8 +1233,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         if (tiles < 256 && ng >= 64 && p.splits == 1)
             p.splits = int(std::min<int64_t>((512 + tiles - 1) / tiles, ng / 16));
     }
-    if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
-        if (env[0] != '\0') {
+    const std::string tune = tuning(kTuneGemm);
+    if (!tune.empty()) {
+        const char* env = tune.c_str();
+        {
             int a = 0, b = 0, c = 0, d = 0, e = 4, sp = 1;
             char fam[16] = {0};
             const int nf =
@@ -1344,8 +1354,8 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
 // wave's K range fits kFusedGroups groups (K <= 8192 with 16 waves); other
 // shapes run the quantizer into the workspace, then the GEMM. (The fused
 // kernel takes up to 16 tokens when forced.)
-// QOQ_GEMM_CONFIG="fused,KW" forces the fused kernel with KW waves; any other
-// family forces the two-call path with that GEMM configuration.
+// The "gemm" tuning value "fused,KW" forces the fused kernel with KW waves;
+// any other family forces the two-call path with that GEMM configuration.
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     LinearPlan p{};
     p.valid = true;
@@ -1357,8 +1367,10 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     const bool pays = M <= 8;
     int kw = ng <= 4 * kFusedGroups ? 4 : (ng <= 8 * kFusedGroups ? 8 : 16);
     bool fused = fits && pays;
-    if (const char* env = std::getenv("QOQ_GEMM_CONFIG")) {
-        if (env[0] != '\0') {
+    const std::string tune = tuning(kTuneGemm);
+    if (!tune.empty()) {
+        const char* env = tune.c_str();
+        {
             int a = 0;
             char fam[16] = {0};
             const int nf = std::sscanf(env, "%15[a-z0-9],%d", fam, &a);

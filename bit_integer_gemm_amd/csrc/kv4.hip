@@ -719,17 +719,18 @@ int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C) { return B * Hkv * C 
 // a second kernel. (Measured on MI355X: cutting every context into fixed
 // 256-1024-token splits to even out ragged lengths is slower -- the
 // per-workgroup query set-up and merge cost more than the imbalance.)
-// QOQ_KV4_SPLITS=<n> forces n splits. Unsplit batches of 2..256 sequences
-// whose pairs fit one per CU take the paired schedule (8-wave workgroups);
-// QOQ_KV4_PAIRED=0 turns it off.
+// The "kv4_splits" tuning key forces n splits. Unsplit batches of 2..256
+// sequences whose pairs fit one per CU take the paired schedule (8-wave
+// workgroups); the "kv4_paired" key set to "0" turns it off.
 Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     Kv4Plan p{};
     const int64_t nb = std::max<int64_t>(1, (max_len + kBlk - 1) / kBlk);
     const int64_t regions = std::max<int64_t>(1, B * Hkv);
     int64_t splits = (512 + regions - 1) / regions;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (nb + 3) / 4));
-    if (const char* env = std::getenv("QOQ_KV4_SPLITS")) {
-        const int v = std::atoi(env);
+    const std::string tune_splits = tuning(kTuneKv4Splits);
+    if (!tune_splits.empty()) {
+        const int v = std::atoi(tune_splits.c_str());
         if (v > 0) splits = std::min(v, 1 << 16);
     }
     p.splits = int(splits);
@@ -740,8 +741,7 @@ Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     // would run two contexts back to back per 4-wave workgroup, which costs
     // the fp16 cache more than it saves: 121 -> 133 us on 16 x 64 heads)
     p.paired = splits == 1 && B >= 2 && B <= kPairMaxB && (B + 1) / 2 * Hkv <= 256;
-    if (const char* env = std::getenv("QOQ_KV4_PAIRED"))
-        if (env[0] == '0') p.paired = false;
+    if (tuning(kTuneKv4Paired) == "0") p.paired = false;
     if (p.paired) {
         p.grid = (B + 1) / 2 * Hkv;
         p.waves = 8;

@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
 #include <tuple>
 #include <utility>
 
@@ -60,6 +61,11 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
     return launch_tuple(kernel, grid, block, shmem, stream, tup,
                         std::index_sequence_for<KArgs...>{});
 }
+
+// Plan overrides for measurements and tests (qoq_set_tuning): the value of
+// a key, or "" when it is unset. Read by the planners on the host.
+enum TuningKey { kTuneGemm = 0, kTuneVariant, kTuneKv4Splits, kTuneKv4Paired, kTuneCount };
+std::string tuning(TuningKey key);
 
 constexpr int kGroup = 128;
 constexpr int kBlockCols = 16;
@@ -157,7 +163,7 @@ hipError_t launch_stream(const GemmPlan& p, const GemmArgs& a, int32_t* part, hi
 // either one fused launch (small M) or the quantizer into a workspace
 // followed by the GEMM.
 struct LinearPlan {
-    bool valid;         // false: QOQ_GEMM_CONFIG names no usable configuration
+    bool valid;         // false: the "gemm" tuning names no usable configuration
     bool fused;         // one launch, every workgroup quantizes the tokens itself
     int kw;             // fused: waves splitting K
     int grid_x;
@@ -180,7 +186,7 @@ constexpr int kVariantW8A8 = 1;
 constexpr int kVariantW4A4 = 2;
 constexpr int kVariantW4A16 = 3;
 struct VariantPlan {
-    bool valid;         // false: QOQ_VARIANT_CONFIG names no compiled configuration
+    bool valid;         // false: the "variant" tuning names no compiled configuration
     int fmt;
     int mt, cb, pb, pa, nw;
     int grid_x;

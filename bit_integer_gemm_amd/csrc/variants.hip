@@ -766,8 +766,8 @@ bool variant_config_exists(int mt, int cb, int pb, int minb, int nw) {
 
 // Launch plan of the comparison GEMMs: W8A8 takes the W4A8 plan's 32x32
 // tile when it is compiled for it; W4A4 (twice the accumulators) uses
-// 64-row tiles. QOQ_VARIANT_CONFIG="MT,CB,PB,WGPERCU,NW" forces one compiled
-// configuration; anything else is an error.
+// 64-row tiles. The "variant" tuning key "MT,CB,PB,WGPERCU,NW" forces one
+// compiled configuration; anything else is an error.
 VariantPlan plan_variant(int fmt, int64_t M, int64_t N, int64_t K) {
     VariantPlan p{};
     p.valid = true;
@@ -790,8 +790,10 @@ VariantPlan plan_variant(int fmt, int64_t M, int64_t N, int64_t K) {
     } else {
         p.mt = 2; p.cb = 1; p.pb = w8 ? 4 : 2; p.pa = 2; p.nw = 4;
     }
-    if (const char* env = std::getenv("QOQ_VARIANT_CONFIG")) {
-        if (env[0] != '\0') {
+    const std::string tune = tuning(kTuneVariant);
+    if (!tune.empty()) {
+        const char* env = tune.c_str();
+        {
             int a = 0, b = 0, c = 0, d = 0, e = 0;
             const int nf = std::sscanf(env, "%d,%d,%d,%d,%d", &a, &b, &c, &d, &e);
             if (nf != 5 || !exists(a, b, c, d, e)) {

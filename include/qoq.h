@@ -33,8 +33,11 @@
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified
  *     (but every memory access stays in bounds: indices depend on shapes
  *     only).
- *   - The library keeps no mutable global state; calls on different
- *     streams are independent unless they share an output or a workspace.
+ *   - The library keeps no mutable global state except the tuning
+ *     overrides of qoq_set_tuning (a measurement and test aid, unset by
+ *     default) and the scratch addresses of qoq_w4a8_gemm_noalloc; calls on
+ *     different streams are independent unless they share an output, a
+ *     workspace or (no-alloc calls) a GPU's scratch array.
  */
 #ifndef QOQ_H
 #define QOQ_H
@@ -55,7 +58,8 @@ typedef enum qoq_status {
     QOQ_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required         */
     QOQ_ERR_HIP = 6,       /* a kernel launch failed (hipGetLastError)        */
     QOQ_ERR_FLAGS = 7,     /* unknown flag bits                               */
-    QOQ_ERR_CONFIG = 8     /* QOQ_GEMM_CONFIG names no compiled configuration */
+    QOQ_ERR_CONFIG = 8     /* a tuning override names no compiled configuration,
+                              or qoq_set_tuning got an unknown key          */
 } qoq_status;
 
 /* Group size of level 2 (inputs of one output channel per group). */
@@ -168,13 +172,10 @@ size_t qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   workspace    qoq_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
  *                (may be NULL when that is 0).
  * M == 0 launches nothing.
- * Kernel choice: the library picks a kernel family and tile from (M, N, K).
- * The environment variable QOQ_GEMM_CONFIG ("decode,MT,CB,KW,PD",
- * "lds,MT,CB,NW,PD[,SPLITS]", "tile32,MT,CB,PB,WGPERCU[,NW[,SPLITS]]" or
- * "generic,MT,2") forces one compiled configuration for measurements (SPLITS:
- * K ranges over workgroups, 1..64, rounded to whole chunks of 8 groups);
- * every configuration computes the same INT32 accumulators. A value naming no compiled configuration valid
- * for the shape makes the call fail with QOQ_ERR_CONFIG (nothing launched).
+ * Kernel choice: the library picks a kernel family and tile from (M, N, K);
+ * the "gemm" key of qoq_set_tuning forces one compiled configuration for
+ * measurements and tests (see there); every configuration computes the same
+ * INT32 accumulators.
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
  * QOQ_ERR_WORKSPACE, QOQ_ERR_CONFIG, QOQ_ERR_HIP. */
 qoq_status qoq_w4a8_gemm(const int8_t* x8, const float* s_x, int64_t M, int64_t K,
@@ -216,7 +217,7 @@ size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* How qoq_w4a8_linear runs this shape: 1 one fused launch (tokens
  * quantized by every workgroup, no workspace), 0 the quantizer then the
- * GEMM, -1 invalid shape or QOQ_GEMM_CONFIG. Host-only. */
+ * GEMM, -1 invalid shape or "gemm" tuning override. Host-only. */
 int qoq_linear_path(int64_t M, int64_t N, int64_t K);
 
 /* Per-token activation quantization and W4A8 GEMM in one call (run time).
@@ -235,7 +236,7 @@ int qoq_linear_path(int64_t M, int64_t N, int64_t K);
  *   workspace    qoq_linear_workspace_bytes(M, N, K) bytes, 16-byte aligned
  *                (may be NULL when that is 0); overlapping calls must not
  *                share it.
- * QOQ_GEMM_CONFIG="fused,KW" (KW in 4, 8, 16) forces the fused kernel
+ * The "gemm" tuning value "fused,KW" (KW in 4, 8, 16) forces the fused kernel
  * (M <= 16, K <= 512 KW);
  * any other family forces the two-call path with that GEMM configuration.
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_GROUP, QOQ_ERR_ALIGN,
@@ -244,6 +245,26 @@ qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K,
                            const void* packed, const uint16_t* s1, int64_t N, int32_t group,
                            uint16_t* y, int32_t* acc_debug,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Plan overrides for measurements and tests (not for production use): the
+ * library reads no environment variables; these process-wide settings
+ * force a launch configuration instead. value NULL or "" clears a key.
+ *   "gemm"        GEMM plan: "decode,MT,CB,KW,PD", "lds,MT,CB,NW,PD[,SPLITS]",
+ *                 "tile32,MT,CB,PB,WGPERCU[,NW[,SPLITS]]",
+ *                 "ksplit,MT,CB,KW,PD", "wide,MT,CB,NW,R,WGPERCU[,SPLITS]",
+ *                 "stream,MT,CB,NW,PD,CH[,SPLITS]", "generic,MT,2", or (for
+ *                 qoq_w4a8_linear) "fused,KW". SPLITS: K ranges over
+ *                 workgroups, 1..64, rounded to whole chunks of 8 groups.
+ *                 A value naming no compiled configuration valid for the
+ *                 shape makes the GEMM calls fail with QOQ_ERR_CONFIG
+ *                 (nothing launched).
+ *   "variant"     comparison GEMMs (qoq_variants.h): "MT,CB,PB,WGPERCU,NW".
+ *   "kv4_splits"  decode attention (qoq_kv4.h): split count n > 0 (<= 65536).
+ *   "kv4_paired"  decode attention: "0" turns the paired schedule off.
+ * Settings apply to calls made after this one returns; setting a key while
+ * another thread enqueues work races with that thread's plan.
+ * Errors: QOQ_ERR_NULL (key NULL), QOQ_ERR_CONFIG (unknown key). */
+qoq_status qoq_set_tuning(const char* key, const char* value);
 
 /* Static description of a status code (never NULL). */
 const char* qoq_status_string(int status);

@@ -76,8 +76,9 @@ size_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int
  * [H_kv, D], cache as above, lens device int32 [B] (context lengths; values
  * are clamped to [0, min(max_len, capacity)]), max_len host-side bound of
  * the lengths (sets how contexts are split), out [B, H, D] fp16.
- * H % H_kv == 0 and H / H_kv <= 16. QOQ_KV4_SPLITS=<n> forces n splits
- * (at most 65536). QOQ_ERR_SHAPE also when a launch would count 2^32
+ * H % H_kv == 0 and H / H_kv <= 16. The "kv4_splits" key of
+ * qoq_set_tuning forces n splits (at most 65536), "kv4_paired" = "0" turns
+ * the paired schedule off. QOQ_ERR_SHAPE also when a launch would count 2^32
  * work-items or more (B * H >= 2^26, or a forced split count that large).
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN, QOQ_ERR_WORKSPACE,
  * QOQ_ERR_HIP. */
@@ -91,7 +92,7 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, int64_t B, int64_t H, int
  * pages set the 4-bit cache against), 512 bytes per token and KV head
  * (keys and values as stored, in the same MFMA lane order), queries
  * unsmoothed: out = softmax(q . k / sqrt(D)) v. Same shapes, errors,
- * workspace (qoq_kv4_attention_workspace_bytes) and QOQ_KV4_SPLITS as the
+ * workspace (qoq_kv4_attention_workspace_bytes) and tuning keys as the
  * KV4 calls. */
 size_t qoq_kv16_cache_bytes(int64_t B, int64_t H_kv, int64_t capacity, int64_t D);
 qoq_status qoq_kv16_append(const uint16_t* k, const uint16_t* v, int64_t B, int64_t T_new,

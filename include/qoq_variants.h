@@ -29,8 +29,9 @@
  * Conventions as in qoq.h: device pointers owned by the caller, 16-byte
  * alignment of every buffer (checked), shapes checked before any launch,
  * N % 16 == 0, K % 128 == 0, nothing allocated, freed or synchronized, all
- * work enqueued on `stream`. QOQ_VARIANT_CONFIG="MT,CB,PB,WGPERCU,NW" forces
- * one compiled tile configuration of the GEMMs (QOQ_ERR_CONFIG otherwise).
+ * work enqueued on `stream`. The "variant" key of qoq_set_tuning
+ * ("MT,CB,PB,WGPERCU,NW") forces one compiled tile configuration of the
+ * GEMMs (QOQ_ERR_CONFIG otherwise).
  */
 #ifndef QOQ_VARIANTS_H
 #define QOQ_VARIANTS_H

@@ -10,3 +10,16 @@ for p in (ROOT, HERE):
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning_overrides():
+    """Every test starts and ends with the library's default launch plans:
+    tuning overrides (qoq_set_tuning) a test set are cleared afterwards."""
+    yield
+    import bit_integer_gemm_amd as qoq
+    if qoq._LIB is not None:
+        qoq.clear_tuning()

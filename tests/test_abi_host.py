@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_variant_sizes_and_validation(monkeypatch):
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     L = qoq.lib()
     assert L.qoq_w8a8_weight_bytes(4096, 4096) == 4096 * 4096
     assert L.qoq_w8a8_weight_bytes(4008, 4096) == 0
@@ -72,14 +72,14 @@ def test_variant_sizes_and_validation(monkeypatch):
     assert L.qoq_w8a8_gemm(P, P, 4, 1 << 16, P, P, 1 << 15, P, None, None) == SHAPE   # N K = 2^31
     assert L.qoq_w4a4_gemm(P, 4, 1 << 17, P, 1 << 15, P, None) == SHAPE             # N K / 2 = 2^31
     assert L.qoq_w4a16_gemm(P, 4, 1 << 17, P, 1 << 15, P, None) == SHAPE
-    monkeypatch.setenv("QOQ_VARIANT_CONFIG", "9,9,9,9,9")
+    qoq.set_tuning("variant", "9,9,9,9,9")
     assert L.qoq_w8a8_gemm(P, P, 4, 4096, P, P, 4096, P, None, None) == 8
     assert L.qoq_w4a4_gemm(P, 4, 4096, P, 4096, P, None) == 8
     assert L.qoq_w4a16_gemm(P, 4, 4096, P, 4096, P, None) == 8
 
 
 def test_kv4_sizes_and_validation(monkeypatch):
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     L = qoq.lib()
     assert L.qoq_kv4_cache_bytes(64, 8, 2048, 128) == 64 * 8 * 2048 * 133
     assert L.qoq_kv4_cache_bytes(2, 8, 100, 128) == 0          # capacity not a multiple of 32
@@ -92,9 +92,9 @@ def test_kv4_sizes_and_validation(monkeypatch):
     # results (132 floats per query head and split) meet in the workspace
     assert L.qoq_kv4_attention_workspace_bytes(64, 32, 8, 128, 2048) == 0
     assert L.qoq_kv4_attention_workspace_bytes(4, 32, 8, 128, 16384) == 4 * 32 * 16 * 132 * 4
-    monkeypatch.setenv("QOQ_KV4_SPLITS", "3")
+    qoq.set_tuning("kv4_splits", "3")
     assert L.qoq_kv4_attention_workspace_bytes(4, 32, 8, 128, 16384) == 4 * 32 * 3 * 132 * 4
-    monkeypatch.delenv("QOQ_KV4_SPLITS")
+    qoq.set_tuning("kv4_splits", None)
     att = L.qoq_kv4_decode_attention
     assert att(P, 2, 32, 8, 64, P, P, 64, P, 64, P, None, 0, None) == SHAPE      # D
     assert att(P, 2, 30, 8, 128, P, P, 64, P, 64, P, None, 0, None) == SHAPE     # H % H_kv
@@ -114,9 +114,9 @@ def test_kv4_sizes_and_validation(monkeypatch):
     assert L.qoq_kv16_decode_attention(P, 1 << 20, 64, 64, 128, P, 32, P, 32, P, None, 0,
                                        None) == SHAPE
     assert L.qoq_kv4_attention_workspace_bytes(1 << 20, 64, 64, 128, 32) == 0
-    monkeypatch.setenv("QOQ_KV4_SPLITS", "1000000000")   # clamped to 2^16 splits
+    qoq.set_tuning("kv4_splits", "1000000000")   # clamped to 2^16 splits
     assert att(P, 64, 32, 8, 128, P, P, 1 << 20, P, 1 << 20, P, None, 0, None) == SHAPE
-    monkeypatch.delenv("QOQ_KV4_SPLITS")
+    qoq.set_tuning("kv4_splits", None)
     app = L.qoq_kv4_append
     assert app(P, P, 2, 0, 8, 128, P, P, P, 64, None) == OK
     assert app(P, P, 2, 5, 8, 128, P, None, P, 64, None) == NULL
@@ -190,7 +190,7 @@ def test_split_k_workspace_bytes(monkeypatch):
                                  ("lds,4,1,4,2,1", 64, 528, 2560, 1),
                                  ("tile32,2,1,2,2,4,3", 64, 528, 2560, 3),
                                  ("tile32,4,1,2,1,8,2", 300, 1040, 1152, 2)]:   # 8 + 1
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+        qoq.set_tuning("gemm", cfg)
         want = splits * M * N * 4 if splits > 1 else 0
         assert qoq.qoq_gemm_workspace_bytes(M, N, K) == want, cfg
         # the two-call linear path carves the same partials after x8 and s_x
@@ -198,7 +198,7 @@ def test_split_k_workspace_bytes(monkeypatch):
         assert qoq.qoq_linear_workspace_bytes(M, N, K) == act + want, cfg
     for bad in ("lds,4,1,4,2,0", "lds,4,1,4,2,65", "lds,4,3,4,2,2", "tile32,2,1,2,2,4,0",
                 "tile32,2,1,2,2,4,65"):
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        qoq.set_tuning("gemm", bad)
         assert qoq.qoq_gemm_workspace_bytes(64, 528, 2560) == 0
         assert qoq.qoq_w4a8_gemm(P, P, 64, 2560, P, P, 528, 128, P, None, None, 0, None) == 8
 
@@ -215,15 +215,14 @@ def test_stream_read_rejects_bad_arguments():
 def test_default_plans_split_long_k(monkeypatch):
     """The planner splits K for long-K shapes over few output tiles (the
     workspace then holds splits x M x N INT32 partials) and nowhere else."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     ws = qoq.qoq_gemm_workspace_bytes
     assert ws(64, 8192, 24576) == 4 * 64 * 8192 * 4          # Qwen1.5-72B down, M = 64
-    assert ws(64, 24576, 8192) == 2 * 64 * 24576 * 4         # Qwen1.5-72B qkv, M = 64
     assert ws(1024, 8192, 24576) == 2 * 1024 * 8192 * 4      # Qwen1.5-72B down, M = 1024
     for M, N, K in [(1, 4096, 4096), (8, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
                     (64, 49152, 8192), (256, 6144, 4096), (256, 4096, 4096), (256, 28672, 4096),
                     (4096, 14336, 4096), (1024, 49152, 8192), (1024, 24576, 8192), (16, 512, 512),
-                    (256, 4096, 14336)]:
+                    (256, 4096, 14336), (64, 24576, 8192)]:
         assert ws(M, N, K) == 0, (M, N, K)
 
 
@@ -299,20 +298,20 @@ def test_linear_workspace_bytes():
 
 
 def test_linear_path(monkeypatch):
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     # one fused launch for M <= 8 with K <= 8192, otherwise two launches
     assert [qoq.qoq_linear_path(M, 4096, 4096) for M in (1, 8, 9, 64, 256)] == [1, 1, 0, 0, 0]
     assert qoq.qoq_linear_path(8, 4096, 16384) == 0
     assert qoq.qoq_linear_path(0, 4096, 4096) == -1 and qoq.qoq_linear_path(4, 4008, 4096) == -1
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,16")
+    qoq.set_tuning("gemm", "fused,16")
     assert qoq.qoq_linear_path(16, 4096, 8192) == 1
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "decode,2,1,8,4")         # 2 row tiles, 13 column tiles
+    qoq.set_tuning("gemm", "decode,2,1,8,4")         # 2 row tiles, 13 column tiles
     assert qoq.qoq_linear_path(64, 208, 4096) == -1
     assert qoq.qoq_linear_path(64, 256, 4096) == 0
 
 
 def test_linear_rejects_bad_arguments(monkeypatch):
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     f = qoq.qoq_w4a8_linear
     args = dict(x=P, M=4, K=4096, packed=P, s1=P, N=4096, group=128, y=P,
                 acc_debug=None, workspace=None, workspace_bytes=0, stream=None)
@@ -337,10 +336,10 @@ def test_linear_rejects_bad_arguments(monkeypatch):
     assert call(M=64, workspace=P, workspace_bytes=need - 1) == WORKSPACE
     assert call(M=64, workspace=P + 8, workspace_bytes=need) == ALIGN
     # the fused kernel cannot take 64 tokens: a forced fused configuration is refused
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,8")
+    qoq.set_tuning("gemm", "fused,8")
     assert call(M=64, workspace=P, workspace_bytes=need) == 8
     assert call(M=4, K=16384) == 8          # 128 groups do not fit 8 waves x 4 groups
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "fused,5")
+    qoq.set_tuning("gemm", "fused,5")
     assert call() == 8
 
 
@@ -355,7 +354,7 @@ def test_binding_refuses_cpu_tensors():
 def test_unknown_kernel_override_is_rejected_before_launch(monkeypatch):
     f = qoq.qoq_w4a8_gemm
     for bad in ("tile32,99,1,1,1", "nonsense", "decode,9,9,9,9"):
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        qoq.set_tuning("gemm", bad)
         assert f(P, P, 4, 4096, P, P, 4096, 128, P, None, None, 0, None) == 8
         assert qoq.qoq_gemm_workspace_bytes(4, 4096, 4096) == 0
 
@@ -404,3 +403,22 @@ def test_launch_failure_reports_hip_error():
     assert qoq.qoq_pack_weights(P, 16, 128, 128, P, P, None, 0, None) == HIP
     # the allocation-free GEMM fails already when it looks up its scratch array
     assert qoq.qoq_w4a8_gemm_noalloc(P, P, 64, 16384, P, P, 4096, 128, P, None, None) == HIP
+
+
+def test_tuning_keys_and_errors():
+    """Plan overrides go through qoq_set_tuning only (no environment
+    variable is read): unknown keys and a NULL key are refused; a set
+    override is used by the next call and cleared by an empty value."""
+    L = qoq.lib()
+    assert L.qoq_set_tuning(None, b"x") == NULL
+    assert L.qoq_set_tuning(b"nonsense", b"1") == 8
+    os.environ["QOQ_GEMM_CONFIG"] = "nonsense"          # ignored by the library
+    try:
+        assert qoq.qoq_gemm_workspace_bytes(64, 528, 2560) == 0
+        qoq.set_tuning("gemm", "lds,4,1,4,2,3")
+        assert qoq.qoq_gemm_workspace_bytes(64, 528, 2560) == 3 * 64 * 528 * 4
+        qoq.set_tuning("gemm", "")
+        assert qoq.qoq_gemm_workspace_bytes(64, 528, 2560) == 0
+    finally:
+        del os.environ["QOQ_GEMM_CONFIG"]
+        qoq.clear_tuning()

@@ -1,6 +1,6 @@
 """Every compiled GEMM kernel configuration against the oracle.
 
-The library picks a kernel family and tile per shape; QOQ_GEMM_CONFIG forces
+The library picks a kernel family and tile per shape; the "gemm" tuning override forces
 one configuration (a name that is not compiled makes the call fail, so a
 silently ignored override cannot pass). Each configuration must give the
 oracle's INT32 accumulators bit-exactly on ragged shapes (odd group counts,
@@ -80,7 +80,7 @@ def _run(monkeypatch, cfg, M, K, N):
     tolerance, and nothing written outside y, the accumulators or the
     workspace (guard bands on all three)."""
     pw, x8, s_x, ref = _case(M, K, N)
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+    qoq.set_tuning("gemm", cfg)
     print(f"\n[gpu-case] {cfg} M={M} K={K} N={N}", flush=True)
     gy = Guarded((M, N), torch.float16, DEV)
     gacc = Guarded((M, N), torch.int32, DEV)
@@ -126,7 +126,7 @@ def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
     """Short, narrow layers at 65-128 tokens take the decode family by
     default (64-row tiles paired 8 workgroup ids apart), including fewer
     groups than waves."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
     y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
@@ -145,7 +145,23 @@ def test_ksplit_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
     that is closer to one workgroup per CU (N = 6144, 8192); ragged rows
     (M = 129, 193, 200), fewer groups than waves (K = 256 / 384), odd
     column counts (N = 2064: the last 32-column tile half outside)."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("M,K,N", [(40, 4096, 18432), (64, 5120, 30720)])
+def test_ksplit_plan_for_wide_layers_at_64_tokens(M, K, N, monkeypatch):
+    """33-64 tokens on layers of 18432-30720 columns with K >= 4096 take the
+    K-split family's 64 x 96 tiles by default (M = 40: rows 40-63 of the
+    tile padded; K = 5120: 40 groups, 10 per wave)."""
+    qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
     y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
@@ -161,7 +177,7 @@ def test_wide_tile_plan_when_tiles_fill_rounds(M, K, N, monkeypatch):
     """Shapes whose 256 x 256 tiles fill whole rounds of the CUs (here 2 x 256
     tiles, the second row tile ragged at 44 rows) take the wide-tile family
     by default."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
     y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
@@ -177,7 +193,7 @@ def test_wide_layer_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
     """Wide layers at 129-256 tokens with at least 192 tiles of 128 x 256
     take those tiles with 8 waves by default (the last row tile ragged for
     M = 200)."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
     y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
@@ -192,7 +208,7 @@ def test_decode_row_tiles_need_whole_rounds(monkeypatch):
     """Row tiles pair workgroups 8 ids apart, which needs the column tiles in
     whole rounds of 8: otherwise the configuration is refused."""
     pw, x8, s_x, _ = _case(*SHAPES_SMALL_M[2])          # M = 37, N = 48: 3 column tiles
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "decode,1,1,8,4")
+    qoq.set_tuning("gemm", "decode,1,1,8,4")
     with pytest.raises(qoq.QoQError) as e:
         qoq.w4a8_gemm(x8, s_x, pw)
     assert e.value.status == 8
@@ -222,7 +238,7 @@ def test_split_k(monkeypatch, fam, cfg, splits):
     by a second kernel that applies the epilogue."""
     name = _fmt(fam, cfg) + f",{splits}"
     for (M, K, N) in SPLITK_SHAPES:
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", name)
+        qoq.set_tuning("gemm", name)
         ng = K // 128
         gps = min(ng, -(-(-(-ng // splits)) // 8) * 8)
         nsplit = -(-ng // gps)
@@ -233,7 +249,7 @@ def test_split_k(monkeypatch, fam, cfg, splits):
 
 def test_split_k_needs_its_workspace(monkeypatch):
     pw, x8, s_x, _ = _case(64, 2560, 528)
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "lds,4,1,4,2,3")
+    qoq.set_tuning("gemm", "lds,4,1,4,2,3")
     need = qoq.qoq_gemm_workspace_bytes(64, 528, 2560)
     assert need == 3 * 64 * 528 * 4
     y = torch.empty((64, 528), dtype=torch.float16, device=DEV)
@@ -263,7 +279,7 @@ def test_generic_family(monkeypatch, cfg):
 def test_unknown_configuration_is_an_error(monkeypatch):
     pw, x8, s_x, _ = _case(*SHAPES_SMALL_M[0])
     for bad in ("tile32,99,1,1,1", "decode,1,3,3,3", "nonsense"):
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", bad)
+        qoq.set_tuning("gemm", bad)
         with pytest.raises(qoq.QoQError) as e:
             qoq.w4a8_gemm(x8, s_x, pw)
         assert e.value.status == 8

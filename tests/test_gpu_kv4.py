@@ -97,11 +97,11 @@ def _tolerance(ref, res, lens):
 
 
 def _run(B, H, Hkv, lens, C, seed, monkeypatch, splits=None, chunks=None):
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     if splits:
-        monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
+        qoq.set_tuning("kv4_splits", str(splits))
     print(f"\n[gpu-case] kv4 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits} "
-          f"paired={os.environ.get('QOQ_KV4_PAIRED', 'default')}",
+          f"paired={qoq.get_tuning('kv4_paired') or 'default'}",
           flush=True)
     q, k, v, lam, lam_d, cache = _build(B, H, Hkv, lens, C, seed, chunks)
     T = k.shape[1]
@@ -124,7 +124,7 @@ def test_cache_offsets_beyond_2_32(fp16, monkeypatch):
     more than 4 GiB into the buffer (64-bit region offsets); short contexts
     keep the oracle small. Appended at the start of every region and, for the
     second sequence, at the far end of its capacity."""
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     B, H, Hkv, C = 2, 32, 8, 1 << 21
     lens = np.array([50, 77], np.int32)
     print(f"\n[gpu-case] kv{'16' if fp16 else '4'} capacity 2^21 B={B} Hkv={Hkv}", flush=True)
@@ -193,7 +193,7 @@ def test_paired_schedule(B, H, Hkv, lens, C, paired, monkeypatch):
     """Unsplit batches of 2..256 sequences whose pairs fit one per CU run two
     contexts of complementary length rank per 8-wave workgroup; the same
     cases with the schedule turned off meet the same bound."""
-    monkeypatch.setenv("QOQ_KV4_PAIRED", paired)
+    qoq.set_tuning("kv4_paired", paired)
     got, res, _ = _run(B, H, Hkv, lens, C, seed=B + 3 * H + C, monkeypatch=monkeypatch)
     for b, n in enumerate(lens):
         if n == 0:
@@ -237,7 +237,7 @@ def test_appends_in_pieces(monkeypatch):
 def test_single_token_context_is_exact(monkeypatch):
     """One cached token: the output is its dequantized value fp16((u - z) s)
     bit for bit, whatever the query."""
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     B, H, Hkv, C = 3, 8, 2, 32
     q, k, v, lam, lam_d, cache = _build(B, H, Hkv, [1, 1, 1], C, seed=29)
     ref = oracle.kv4_encode(k, v, lam)
@@ -249,7 +249,7 @@ def test_single_token_context_is_exact(monkeypatch):
 
 
 def test_zero_query_is_mean(monkeypatch):
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     B, H, Hkv, C = 2, 4, 2, 128
     lens = [100, 37]
     q, k, v, lam, lam_d, cache = _build(B, H, Hkv, lens, C, seed=31)
@@ -273,7 +273,7 @@ def test_workload_sampled_heads(key, monkeypatch):
     contexts of 8-16 K tokens, split over workgroups) at full size, in the
     benchmark's launch configuration, for the 4-bit and the fp16 cache; the
     oracle checks a sample of sequences one by one."""
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     w = wl.ATTN_WORKLOADS[key]
     q, k, v, lens = wl.make_attention_case(w)
     C = int(-(-lens.max() // 32) * 32)
@@ -312,11 +312,11 @@ def test_workload_sampled_heads(key, monkeypatch):
 # the fp16 comparison path
 # ---------------------------------------------------------------------------
 def _run16(B, H, Hkv, lens, C, seed, monkeypatch, splits=None):
-    monkeypatch.delenv("QOQ_KV4_SPLITS", raising=False)
+    qoq.set_tuning("kv4_splits", None)
     if splits:
-        monkeypatch.setenv("QOQ_KV4_SPLITS", str(splits))
+        qoq.set_tuning("kv4_splits", str(splits))
     print(f"\n[gpu-case] kv16 B={B} H={H} Hkv={Hkv} lens={list(lens)} C={C} splits={splits} "
-          f"paired={os.environ.get('QOQ_KV4_PAIRED', 'default')}",
+          f"paired={qoq.get_tuning('kv4_paired') or 'default'}",
           flush=True)
     q, k, v = wl.make_attention(B, H, Hkv, D, lens, seed=seed)
     cache = qoq.kv16_alloc_cache(B, Hkv, C, DEV)
@@ -348,7 +348,7 @@ def test_fp16_attention_parity(B, H, Hkv, lens, C, monkeypatch):
 
 @pytest.mark.parametrize("paired", ["1", "0"])
 def test_fp16_paired_schedule(paired, monkeypatch):
-    monkeypatch.setenv("QOQ_KV4_PAIRED", paired)
+    qoq.set_tuning("kv4_paired", paired)
     _run16(5, 8, 2, [40, 128, 3, 128, 77], 128, seed=31, monkeypatch=monkeypatch)
 
 

@@ -35,11 +35,11 @@ def _check(M, K, N, monkeypatch, cfg=None):
     W, X, _ = wl.make_inputs(M, K, N, seed=7 * M + K + N)
     pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
     xd = _half(X)
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     x8, s_x = qoq.quantize_act(xd)
     y2, acc2 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
     if cfg is not None:
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+        qoq.set_tuning("gemm", cfg)
     print(f"\n[gpu-case] linear cfg={cfg} M={M} K={K} N={N}", flush=True)
     y1, acc1 = qoq.w4a8_linear(xd, pw, acc_debug=True)
     torch.cuda.synchronize()
@@ -76,7 +76,7 @@ def test_forced_two_call_path_for_small_m(monkeypatch):
 
 
 def test_zero_rows_and_empty_batch(monkeypatch):
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     W, X, _ = wl.make_inputs(6, 1024, 96, seed=3)
     X[2] = 0
     X[5] = 0

@@ -263,17 +263,17 @@ def test_workspace_is_reusable(monkeypatch):
     need = []
     for (M, K, N, cfg) in SPLIT_CASES:
         if cfg:
-            monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+            qoq.set_tuning("gemm", cfg)
         else:
-            monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+            qoq.set_tuning("gemm", None)
         need.append(qoq.qoq_gemm_workspace_bytes(M, N, K))
     assert all(b > 0 for b in need), need
     ws = GuardedWorkspace(max(need), DEV)
     for (M, K, N, cfg) in SPLIT_CASES:
         if cfg:
-            monkeypatch.setenv("QOQ_GEMM_CONFIG", cfg)
+            qoq.set_tuning("gemm", cfg)
         else:
-            monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+            qoq.set_tuning("gemm", None)
         _announce("workspace reuse", M, K, N, cfg)
         W, X, _ = wl.make_inputs(M, K, N, seed=3 + M + N)
         pw = qoq.pack_weights(torch.from_numpy(W).to(DEV))
@@ -293,7 +293,7 @@ def test_prefill_full_size_all_outputs(monkeypatch):
     benchmark's launch configuration, every one of its 58.7 M outputs: the
     INT32 accumulators bit-exact against the oracle's exact GEMM (fp64 BLAS
     on the integer codes, exact below 2^53) and y within the tolerance."""
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     w = wl.WORKLOADS["prefill"]
     shape = w.shapes[0]
     M = w.Ms[0]
@@ -327,14 +327,14 @@ def test_workload_full_size_sampled(key, shape_name, M, monkeypatch):
     w = wl.WORKLOADS[key]
     shape = next(s for s in w.shapes if s.name == shape_name)
     _announce("workload", key, shape_name, M, shape.K, shape.N)
-    monkeypatch.delenv("QOQ_GEMM_CONFIG", raising=False)
+    qoq.set_tuning("gemm", None)
     W, X, _ = wl.make_case(w, shape, M)
     pw, x8, s_x, y, acc = gpu_run(W, X)
     err = sampled_check(W, X, pw, x8, s_x, y, acc)
     print(f"[gpu-case] ok max rel err {err:.2e}", flush=True)
     if (key, shape_name, M) in COMMON_TILE_CASES:
         # the benchmark's format comparison also times the common 64 x 128 tile
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", "tile32,2,1,2,2,4")
+        qoq.set_tuning("gemm", "tile32,2,1,2,2,4")
         y2, acc2 = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
         torch.cuda.synchronize()
         sampled_check(W, X, pw, x8, s_x, y2, acc2)

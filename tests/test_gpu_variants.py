@@ -31,11 +31,11 @@ def _half(X):
 
 def _w8(M, K, N, monkeypatch, cfg=None):
     W, X, _ = wl.make_inputs(M, K, N, seed=3 * M + K + N)
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     packed, s = qoq.w8a8_pack_weights(torch.from_numpy(W).to(DEV))
     x8, s_x = qoq.quantize_act(_half(X))
     if cfg:
-        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+        qoq.set_tuning("variant", cfg)
     print(f"\n[gpu-case] w8a8 cfg={cfg} M={M} K={K} N={N}", flush=True)
     y, acc = qoq.w8a8_gemm(x8, s_x, packed, s, N, acc_debug=True)
     torch.cuda.synchronize()
@@ -51,11 +51,11 @@ def _w8(M, K, N, monkeypatch, cfg=None):
 
 def _w4(M, K, N, monkeypatch, cfg=None):
     W, X, _ = wl.make_inputs(M, K, N, seed=5 * M + K + N)
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     packed = qoq.w4a4_pack_weights(torch.from_numpy(W).to(DEV))
     act = qoq.w4a4_quantize_act(_half(X))
     if cfg:
-        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+        qoq.set_tuning("variant", cfg)
     print(f"\n[gpu-case] w4a4 cfg={cfg} M={M} K={K} N={N}", flush=True)
     y = qoq.w4a4_gemm(act, M, K, packed, N)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def test_w4a4_zero_groups(monkeypatch):
     W[3, 128:256] = 0
     X[7, 256:384] = 0
     X[11] = 0
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     packed = qoq.w4a4_pack_weights(torch.from_numpy(W).to(DEV))
     act = qoq.w4a4_quantize_act(_half(X))
     y = qoq.w4a4_gemm(act, 20, 512, packed, 64)
@@ -121,10 +121,10 @@ def _w16_check_weights(packed, ref, N, K):
 def _w16(M, K, N, monkeypatch, cfg=None, W=None, X=None):
     if W is None:
         W, X, _ = wl.make_inputs(M, K, N, seed=7 * M + K + N)
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     packed = qoq.w4a16_pack_weights(torch.from_numpy(W).to(DEV))
     if cfg:
-        monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+        qoq.set_tuning("variant", cfg)
     print(f"\n[gpu-case] w4a16 cfg={cfg} M={M} K={K} N={N}", flush=True)
     y = qoq.w4a16_gemm(_half(X), packed, N)
     torch.cuda.synchronize()
@@ -206,7 +206,7 @@ def test_variants_full_size_sampled(key, sname, M, monkeypatch):
     ref8 = oracle.w8a8_linear(Xs, Ws)
     ref4 = oracle.w4a4_linear(Xs, Ws)
     ref16 = oracle.w4a16_linear(Xs, Ws)
-    monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+    qoq.set_tuning("variant", None)
     Wd = torch.from_numpy(W).to(DEV)
     del W
     xd = _half(X)
@@ -219,7 +219,7 @@ def test_variants_full_size_sampled(key, sname, M, monkeypatch):
     ng = K // 128
     for cfg in (None, "2,1,2,2,4"):
         if cfg:
-            monkeypatch.setenv("QOQ_VARIANT_CONFIG", cfg)
+            qoq.set_tuning("variant", cfg)
         print(f"\n[gpu-case] variants full {key} {sname} M={M} cfg={cfg}", flush=True)
         y8, acc8 = qoq.w8a8_gemm(x8, s_x, p8, s8, N, acc_debug=True)
         y4 = qoq.w4a4_gemm(a4, M, K, p4, N)
@@ -234,4 +234,4 @@ def test_variants_full_size_sampled(key, sname, M, monkeypatch):
         yy = _pick(y16, toks, cols).astype(np.float64)
         tol = 2.0 ** -11 * np.abs(ref16["y"]) + (K + 2) * 2.0 ** -23 * ref16["term_abs"] + 2.0 ** -24
         assert not (np.abs(yy - ref16["y"]) > tol).any(), f"w4a16 {cfg}"
-        monkeypatch.delenv("QOQ_VARIANT_CONFIG", raising=False)
+        qoq.set_tuning("variant", None)

@@ -48,8 +48,19 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5033.2        # dense INT8 MFMA: 256 CU x 8192 ops/clk x 2.4 GHz
 ROTATE_BYTES = 512 << 20       # weight copies per shape: twice the last-level cache
 METRIC = "W4A8 GEMM TOPS + % roofline (HBM at M≤64, INT8 MFMA at M≥1024)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_decode.json")
-GEMM_SOURCE = os.path.join(ROOT, "bit_integer_gemm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_gemm_traffic_decode_step.json")
+CSRC_DIR = os.path.join(ROOT, "bit_integer_gemm_amd", "csrc")
+# the sources whose kernels the decode step launches (the counters are only
+# valid for the kernels they were taken on)
+GEMM_SOURCES = ("gemm.hip", "gemm_ksplit.hip", "gemm_wide.hip", "gemm_stream.hip",
+                "act_quant.hip", "kernel_common.hpp", "qoq_internal.hpp")
+
+
+def gemm_sources_sha256():
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(CSRC_DIR, name), "rb").read())
+    return h.hexdigest()
 
 
 def parse():
@@ -210,13 +221,13 @@ def fused_bytes(M, K, N, group=wl.GROUP):
 
 def traffic_record():
     """HBM bytes per decode GEMM launch from the committed rocprofv3 counter
-    runs, if they were taken on the current GEMM source; else None."""
+    runs, if they were taken on the current GEMM sources (SHA-256 over
+    GEMM_SOURCES); else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != src:
+    if rec.get("gemm_sources_sha256") != gemm_sources_sha256():
         return None
     return rec
 

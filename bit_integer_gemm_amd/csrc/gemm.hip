@@ -841,7 +841,7 @@ __device__ __forceinline__ void act_codes(const uint32_t (&w)[V / 2], float inv,
 //   * The KW partial accumulators are summed in LDS and the epilogue uses
 //     s_x = absmax / 127 as the quantizer stores it: outputs equal the
 //     two-call path's bit for bit.
-template <int V, int T, int KW>
+template <int V, int T, int KW, int CB>
 __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     const uint16_t* __restrict__ x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
@@ -852,7 +852,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     constexpr int RR = 64 / LPR;              // token rows per round
     constexpr int ROWS = RR * T;              // token rows held (>= M)
     static_assert(ROWS <= 16, "at most one 16-row tile");
-    __shared__ v4i red[KW * 64];
+    __shared__ v4i red[KW * CB * 64];
     __shared__ __attribute__((aligned(16))) uint8_t aq[KW][GM * ROWS * kGroup];
     __shared__ uint32_t pmax[KW][ROWS];
     const int lane = threadIdx.x & 63;
@@ -860,15 +860,28 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     const int c = lane & 15;
     const int h = lane >> 4;
     const int ng = K >> 7;
-    const int nb = blockIdx.x;
+    const int nbt = N >> 4;
+    const int nb0 = blockIdx.x * CB;              // first of the CB column blocks
     const int gpw = (ng + KW - 1) / KW;           // <= GM (checked by the launch plan)
     const int gb = min(ng, wave * gpw);
     const int cnt = min(ng, gb + gpw) - gb;
 
-    const uint8_t* bptr = nib + int64_t(nb) * ng * kBlockBytes + lane * 16;
-    const uint8_t* rptr = rec + (int64_t(nb) * ng8 * kBlockCols + c) * (kRecChunk * 2);
-    // the channel scale of this thread's epilogue element, fetched now
-    const float esw = h2f(s1[16 * nb + (threadIdx.x & 15)]);
+    const uint8_t* bptr[CB];
+    const uint8_t* rptr[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t nbc = min(nb0 + cb, nbt - 1);   // past N: never stored
+        bptr[cb] = nib + nbc * ng * kBlockBytes + lane * 16;
+        rptr[cb] = rec + (nbc * ng8 * kBlockCols + c) * (kRecChunk * 2);
+    }
+    // the channel scales of this thread's epilogue elements, fetched now
+    constexpr int EI = (256 * CB + 64 * KW - 1) / (64 * KW);
+    float esw[EI];
+#pragma unroll
+    for (int it = 0; it < EI; ++it) {
+        const int e = min(int(threadIdx.x) + it * 64 * KW, 256 * CB - 1);
+        esw[it] = h2f(s1[16 * min(nb0 + (e >> 8), nbt - 1) + (e & 15)]);
+    }
     const int qj = lane % LPR;                    // V-value chunk within the group
     int qrow[T];
 #pragma unroll
@@ -879,8 +892,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     // range repeat its last group (cache hits, never used) -- so the
     // compiler's waits count exactly the loads issued.
     uint32_t xv[T][GM][V / 2];
-    uint4 qn[GM];
-    uint32_t rs[GM];
+    uint4 qn[GM][CB];
+    uint32_t rs[GM][CB];
 #pragma unroll
     for (int i = 0; i < GM; ++i) {
         {
@@ -904,9 +917,12 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     for (int i = 0; i < GM; ++i) {
         {
             const int g = min(gb + i, ng - 1);
-            qn[i] = *reinterpret_cast<const uint4*>(bptr + int64_t(g) * kBlockBytes);
-            rs[i] = *reinterpret_cast<const uint16_t*>(
-                rptr + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                qn[i][cb] = *reinterpret_cast<const uint4*>(bptr[cb] + int64_t(g) * kBlockBytes);
+                rs[i][cb] = *reinterpret_cast<const uint16_t*>(
+                    rptr[cb] + (g >> 3) * (kBlockCols * kRecChunk * 2) + (g & 7) * 2);
+            }
         }
     }
     // token absmax on the magnitude bits (for finite fp16 their order is
@@ -962,44 +978,55 @@ __global__ void __launch_bounds__(64 * KW) gemm_fused_small_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int arow = min(c, M - 1);
-    v4i acc = v4i{0, 0, 0, 0};
+    v4i acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < GM; ++i) {
         if (i < cnt) {
             const uint8_t* src = my + (i * ROWS + arow) * kGroup + 16 * h;
             const v4i a0 = *reinterpret_cast<const v4i*>(src);
             const v4i a1 = *reinterpret_cast<const v4i*>(src + 64);
-            v4i b0, b1;
-            dequant_block(qn[i], rs[i], b0, b1);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                v4i b0, b1;
+                dequant_block(qn[i][cb], rs[i][cb], b0, b1);
+                acc[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[cb], 0, 0, 0);
+            }
         }
     }
 
-    // sum the KW partial accumulators in LDS, then the epilogue (token
-    // 4h + r, channel 16 nb + c for lane (c, h), register r)
-    red[wave * 64 + lane] = acc;
+    // sum the KW partial accumulators in LDS, then the epilogue (column
+    // block cb, token 4h + r, channel 16 (nb0 + cb) + c for lane (c, h),
+    // register r)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) red[(wave * CB + cb) * 64 + lane] = acc[cb];
     __syncthreads();
     const int* redi = reinterpret_cast<const int*>(red);
-    for (int e = threadIdx.x; e < 256; e += 64 * KW) {
+#pragma unroll
+    for (int it = 0; it < EI; ++it) {
+        const int e = int(threadIdx.x) + it * 64 * KW;
+        if (e >= 256 * CB) break;
         const int cc = e & 15;
         const int hh = (e >> 4) & 3;
-        const int rr = e >> 6;
+        const int rr = (e >> 6) & 3;
+        const int cb = e >> 8;
         const int m = 4 * hh + rr;
-        if (m >= M) continue;
+        if (m >= M || nb0 + cb >= nbt) continue;
         const int l = cc + 16 * hh;
         int32_t sum = 0;
         uint32_t mm = 0;
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
-            sum += redi[(w * 64 + l) * 4 + rr];
+            sum += redi[((w * CB + cb) * 64 + l) * 4 + rr];
             mm = max(mm, pmax[w][m]);
         }
         const float am = h2f(uint16_t(mm));
         const float sx = am > 0.0f ? am / float(kActMax) : 0.0f;
-        const int n = 16 * nb + cc;
+        const int n = 16 * (nb0 + cb) + cc;
         if (acc_debug) acc_debug[int64_t(m) * N + n] = sum;
-        y[int64_t(m) * N + n] = epilogue_value(sum, sx, esw);
+        y[int64_t(m) * N + n] = epilogue_value(sum, sx, esw[it]);
     }
 }
 
@@ -1367,18 +1394,22 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     const bool pays = M <= 8;
     int kw = ng <= 4 * kFusedGroups ? 4 : (ng <= 8 * kFusedGroups ? 8 : 16);
     bool fused = fits && pays;
+    int fcb = 1;   // column blocks per fused workgroup
     const std::string tune = tuning(kTuneGemm);
     if (!tune.empty()) {
         const char* env = tune.c_str();
         {
             int a = 0;
             char fam[16] = {0};
-            const int nf = std::sscanf(env, "%15[a-z0-9],%d", fam, &a);
+            int cbf = 1;
+            const int nf = std::sscanf(env, "%15[a-z0-9],%d,%d", fam, &a, &cbf);
             if (std::string(fam) == "fused") {
                 fused = true;
                 kw = a;
-                if (nf != 2 || !fits || (a != 4 && a != 8 && a != 16) ||
-                    ng > int64_t(kFusedGroups) * a) {
+                fcb = cbf;
+                if ((nf != 2 && nf != 3) || !fits || (a != 4 && a != 8 && a != 16) ||
+                    (cbf != 1 && cbf != 2) || ng > int64_t(kFusedGroups) * a ||
+                    (cbf == 2 && a == 16 && M > 12)) {   // not built: LDS above 160 KiB
                     p.valid = false;
                     return p;
                 }
@@ -1390,7 +1421,8 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     if (fused) {
         p.fused = true;
         p.kw = kw;
-        p.grid_x = int(N / kBlockCols);
+        p.fcb = fcb;
+        p.grid_x = int((N / kBlockCols + fcb - 1) / fcb);
         p.ws_bytes = 0;
         return p;
     }
@@ -1407,23 +1439,37 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+template <int V, int T, int CB>
+hipError_t launch_fused_vtc(const LinearPlan& p, const uint16_t* x, int M, int K, const uint8_t* nib,
+                            const uint8_t* rec, int ng8, const uint16_t* s1, int N, uint16_t* y,
+                            int32_t* acc_debug, hipStream_t stream) {
+    switch (p.kw) {
+        case 4:
+            return launch_kernel(gemm_fused_small_kernel<V, T, 4, CB>, dim3(p.grid_x), dim3(256), 0,
+                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
+        case 8:
+            return launch_kernel(gemm_fused_small_kernel<V, T, 8, CB>, dim3(p.grid_x), dim3(512), 0,
+                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
+        case 16:
+            // 16 waves of 16 token rows and two column blocks need more than
+            // the 160 KiB of LDS: not built
+            if constexpr (T == 4 && CB == 2) return hipErrorInvalidConfiguration;
+            else
+                return launch_kernel(gemm_fused_small_kernel<V, T, 16, CB>, dim3(p.grid_x),
+                                     dim3(1024), 0, stream, x, M, K, nib, rec, ng8, s1, N, y,
+                                     acc_debug);
+        default:
+            return hipErrorInvalidConfiguration;
+    }
+}
+
 template <int V, int T>
 hipError_t launch_fused_vt(const LinearPlan& p, const uint16_t* x, int M, int K, const uint8_t* nib,
                            const uint8_t* rec, int ng8, const uint16_t* s1, int N, uint16_t* y,
                            int32_t* acc_debug, hipStream_t stream) {
-    switch (p.kw) {
-        case 4:
-            return launch_kernel(gemm_fused_small_kernel<V, T, 4>, dim3(p.grid_x), dim3(256), 0,
-                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
-        case 8:
-            return launch_kernel(gemm_fused_small_kernel<V, T, 8>, dim3(p.grid_x), dim3(512), 0,
-                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
-        case 16:
-            return launch_kernel(gemm_fused_small_kernel<V, T, 16>, dim3(p.grid_x), dim3(1024), 0,
-                                 stream, x, M, K, nib, rec, ng8, s1, N, y, acc_debug);
-        default:
-            return hipErrorInvalidConfiguration;
-    }
+    if (p.fcb == 2)
+        return launch_fused_vtc<V, T, 2>(p, x, M, K, nib, rec, ng8, s1, N, y, acc_debug, stream);
+    return launch_fused_vtc<V, T, 1>(p, x, M, K, nib, rec, ng8, s1, N, y, acc_debug, stream);
 }
 
 hipError_t launch_linear_fused(const LinearPlan& p, const uint16_t* x, int64_t M, int64_t K,

@@ -166,6 +166,7 @@ struct LinearPlan {
     bool valid;         // false: the "gemm" tuning names no usable configuration
     bool fused;         // one launch, every workgroup quantizes the tokens itself
     int kw;             // fused: waves splitting K
+    int fcb;            // fused: 16-column blocks per workgroup (1 or 2)
     int grid_x;
     int64_t x8_offset, sx_offset, gemm_ws_offset;   // workspace carve-up (two-call path)
     int64_t ws_bytes;

@@ -65,6 +65,23 @@ def test_fused_every_wave_count(kw, monkeypatch):
             _check(M, K, N, monkeypatch, cfg=f"fused,{kw}")
 
 
+@pytest.mark.parametrize("kw", [4, 8, 16])
+def test_fused_two_column_blocks_per_workgroup(kw, monkeypatch):
+    """Workgroups of two 16-channel blocks (half as many workgroups repeat the
+    token quantization), including a column count with an odd number of
+    blocks (N = 400, 208: the last workgroup's second block lies past N)."""
+    for (M, K, N) in FORCED:
+        if K // 128 <= 4 * kw and not (kw == 16 and M > 12):
+            _check(M, K, N, monkeypatch, cfg=f"fused,{kw},2")
+
+
+def test_fused_configuration_out_of_lds_is_refused(monkeypatch):
+    """16 waves of 16 token rows with two column blocks would need more than
+    160 KiB of LDS: the plan refuses it (nothing launched)."""
+    qoq.set_tuning("gemm", "fused,16,2")
+    assert qoq.qoq_linear_path(13, 1040, 2048) == -1
+
+
 @pytest.mark.parametrize("M,K,N", TWO_CALL)
 def test_two_call_path(M, K, N, monkeypatch):
     assert qoq.qoq_linear_workspace_bytes(M, N, K) > 0

@@ -342,7 +342,7 @@ qoq_status qoq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const void* p
 // KV4 decode attention
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int64_t kKv4MaxCapacity = int64_t(1) << 24;
+using qoq::kKv4MaxCapacity;
 
 qoq_status check_kv4_heads(int64_t B, int64_t H, int64_t Hkv, int64_t D) {
     if (D != 128 || B < 0 || B > kMaxDim || Hkv <= 0 || Hkv > 4096 || H <= 0 || H % Hkv != 0 ||

@@ -54,6 +54,9 @@ constexpr int kBlk = 32;                 // tokens per block
 constexpr int kBlkBytes = 2048;          // 32 tokens x 128 dims x 4 bits
 constexpr int kMetaBlkBytes = 160;       // per 32 tokens: 2 x 32 fp16 + 32 bytes
 constexpr int kRegionPerToken = kD + kMetaBlkBytes / kBlk;   // 133
+// the attention addresses a region's key and value codes with 32-bit
+// buffer offsets
+static_assert(kKv4MaxCapacity / kBlk * kBlkBytes <= INT32_MAX, "32-bit offsets");
 
 __device__ __forceinline__ int64_t region_offset(int64_t region, int64_t C) {
     return region * C * kRegionPerToken;
@@ -249,6 +252,20 @@ __device__ __forceinline__ v8h join(const h2 (&r)[4]) {
     return o;
 }
 
+// Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
+// that hold one query's scores) with gfx950's row swaps: swapping the upper
+// 32 lanes of one copy with the lower 32 of another leaves x[l] and
+// x[l ^ 32] in the two results of every lane, and the 16-lane row swap does
+// the same for l ^ 16; no LDS round trip.
+__device__ __forceinline__ float group_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
 struct AttnArgs {
     const uint16_t* q;         // [B, H, D]
     const uint16_t* lam;       // [Hkv, D]
@@ -282,6 +299,10 @@ constexpr int kPairMaxB = 256;
 template <bool kF16, int NW>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kF16 ? 1 : 3)))
 kv4_attention_kernel(AttnArgs a) {
+    // blocks a wave holds in registers: the next block's loads are in flight
+    // while one is computed (deeper rings, 3-5 blocks, measured slower on
+    // every benchmarked batch: more registers, no latency left to hide)
+    constexpr int R = 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15;          // query of the group (MFMA column)
@@ -293,9 +314,11 @@ kv4_attention_kernel(AttnArgs a) {
     auto clamped_len = [&](int b) { return int(min(int64_t(max(min(a.lens[b], a.max_len), 0)), C)); };
 
   // one (sequence, KV head, split): the whole attention of its queries
-  auto run = [&](const int b, const int h, const int sp) {
+  auto run = [&](const int b_in, const int h, const int sp) {
+    // b comes from LDS in the paired schedule: the same in every lane
+    const int b = __builtin_amdgcn_readfirstlane(b_in);
     const int region = b * a.Hkv + h;
-    const int len = clamped_len(b);
+    const int len = __builtin_amdgcn_readfirstlane(clamped_len(b));
     const int nb = (len + kBlk - 1) / kBlk;
     const int blk0 = sp * a.bps;
     const int blk1 = min(nb, blk0 + a.bps);
@@ -343,6 +366,15 @@ kv4_attention_kernel(AttnArgs a) {
 
     auto kofs = [&](int tile) { return (tile * 4 + g) * 256 + j * 16; };
     const int vofs = (g * 16 + j) * 32;
+    // 4-bit cache sections of the region as buffers (key and value codes at
+    // most 2^24 / 32 blocks x 2 KiB = 1 GiB each: 32-bit offsets)
+    const int64_t nblk = C / kBlk;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kbase, (short)0, int(nblk * kBlkBytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)vbase, (short)0, int(nblk * kBlkBytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)mbase, (short)0, int(nblk * kMetaBlkBytes), 0x00020000);
     // per block: key codes (2 tiles), value codes, and the lane's 8 entries
     // of each metadata array (s_k, s_v, zero bytes); or the fp16 operands
     struct Blk4 {
@@ -367,16 +399,17 @@ kv4_attention_kernel(AttnArgs a) {
         for (int c = 0; c < 8; ++c)
             r.v[c] = *reinterpret_cast<const uint4*>(vb + (g * 16 + j) * 128 + 16 * c);
       } else {
-        const uint8_t* kb = kbase + int64_t(blk) * kBlkBytes;
-        const uint8_t* vb = vbase + int64_t(blk) * kBlkBytes;
-        const uint8_t* mb = mbase + int64_t(blk) * kMetaBlkBytes;
-        r.k0 = *reinterpret_cast<const uint4*>(kb + kofs(0));
-        r.k1 = *reinterpret_cast<const uint4*>(kb + kofs(1));
-        r.v0 = *reinterpret_cast<const uint4*>(vb + vofs);
-        r.v1 = *reinterpret_cast<const uint4*>(vb + vofs + 16);
-        r.sk = *reinterpret_cast<const uint4*>(mb + 16 * g);
-        r.sv = *reinterpret_cast<const uint4*>(mb + 64 + 16 * g);
-        r.z = *reinterpret_cast<const uint2*>(mb + 128 + 8 * g);
+        // buffer loads: the lane offsets are fixed, the block offset is
+        // uniform (an SGPR), so no address arithmetic runs per block
+        const int sb = blk * kBlkBytes;
+        const int sm = blk * kMetaBlkBytes;
+        r.k0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kofs(0), sb, 0));
+        r.k1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kofs(1), sb, 0));
+        r.v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs, sb, 0));
+        r.v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs + 16, sb, 0));
+        r.sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rm, 16 * g, sm, 0));
+        r.sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rm, 64 + 16 * g, sm, 0));
+        r.z = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rm, 128 + 8 * g, sm, 0));
       }
     };
     const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
@@ -392,8 +425,7 @@ kv4_attention_kernel(AttnArgs a) {
         float bm = zs[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zs[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = group_max(bm);
         const bool grow = bm > m + 8.0f;
         if (__ballot(grow) != 0) {
             const float fac = grow ? __builtin_amdgcn_exp2f(m - bm) : 1.0f;
@@ -442,7 +474,11 @@ kv4_attention_kernel(AttnArgs a) {
         }
     };
     auto compute4 = [&](const Blk4& r, int blk) {
+        // tokens past the context occur only in a context's last block: the
+        // masks are built there alone (a scalar branch), every other block
+        // runs with all 32 tokens kept
         const int tbase = blk * kBlk;
+        const bool partial = tbase + kBlk > len;
         auto valid = [&](int e) {
             const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
             return tbase + tok < len;
@@ -471,10 +507,17 @@ kv4_attention_kernel(AttnArgs a) {
                 const int e = 4 * tile + i;
                 const h2 sk2 = __builtin_bit_cast(h2, skw[e >> 1]);
                 const float zk = float(((tile ? zk47 : zk03) >> (8 * i)) & 0xffu);
-                const float sc = __builtin_fmaf(acc[i], 16777216.0f, -zk * qsum) *
-                                 (float(sk2[e & 1]) * kScale);
-                zs[e] = valid(e) ? sc : -INFINITY;
+                zs[e] = __builtin_fmaf(acc[i], 16777216.0f, -zk * qsum) *
+                        (float(sk2[e & 1]) * kScale);
             }
+        }
+        uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+        if (partial) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zs[e] = valid(e) ? zs[e] : -INFINITY;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr)
+                keep[pr] = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
         }
         const v8h pop = softmax(zs);
         // values: sum_t p_t s_t (u_t - z_t). The token's scale rides on its
@@ -492,8 +535,7 @@ kv4_attention_kernel(AttnArgs a) {
         v8h pv;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t keep = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
-            const h2 ps = h2{pop[2 * pr], pop[2 * pr + 1]} * __builtin_bit_cast(h2, svw[pr] & keep);
+            const h2 ps = h2{pop[2 * pr], pop[2 * pr + 1]} * __builtin_bit_cast(h2, svw[pr] & keep[pr]);
             pv[2 * pr] = ps[0];
             pv[2 * pr + 1] = ps[1];
         }
@@ -508,21 +550,59 @@ kv4_attention_kernel(AttnArgs a) {
         }
     };
     auto compute = [&](const Blk& r, int blk) {
-        if constexpr (kF16) compute16(r, blk);
-        else compute4(r, blk);
+        if constexpr (kF16) {
+            compute16(r, blk);
+        } else {
+            compute4(r, blk);
+        }
     };
 
-    // the wave's blocks: blk0 + wave, + NW, ...; the next block's loads are
-    // in flight while one is computed
-    Blk ra, rb;
-    int bi = blk0 + wave;
-    if (bi < blk1) load(ra, bi);
-    for (; bi < blk1; bi += 2 * NW) {
-        if (bi + NW < blk1) load(rb, bi + NW);
-        compute(ra, bi);
-        if (bi + NW >= blk1) break;
-        if (bi + 2 * NW < blk1) load(ra, bi + 2 * NW);
-        compute(rb, bi + NW);
+    // the wave's blocks: blk0 + wave, + NW, ...; the loads of the next R - 1
+    // blocks are in flight while one is computed. Every step issues its load
+    // (block numbers past the wave's last block are clamped to it: cache
+    // hits, never used), so each compute waits for exactly its own block.
+    const int first = blk0 + wave;
+    if constexpr (kF16) {
+        // the fp16 cache (comparison point): two blocks, the next one's
+        // loads in flight while one is computed
+        Blk ra, rb;
+        int bi = first;
+        if (bi < blk1) load(ra, bi);
+        for (; bi < blk1; bi += 2 * NW) {
+            if (bi + NW < blk1) load(rb, bi + NW);
+            compute(ra, bi);
+            if (bi + NW >= blk1) break;
+            if (bi + 2 * NW < blk1) load(ra, bi + 2 * NW);
+            compute(rb, bi + NW);
+        }
+    } else if (first < blk1) {
+        // 4-bit cache: whole rounds of R blocks run unconditionally; the
+        // last R - 1 or fewer blocks are already in the ring when the rounds
+        // end and are only computed. Each block's loads stay together and in
+        // order (scheduling barriers), so the waits are the same in every
+        // round.
+        Blk ring[R];
+        const int last = blk1 - 1;
+        const int mine = (last - first) / NW + 1;   // blocks of this wave
+#pragma unroll
+        for (int s = 0; s < R - 1; ++s) {
+            load(ring[s], min(first + s * NW, last));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int b = first, i = 0;
+        for (; i + R <= mine; i += R) {
+#pragma unroll
+            for (int s = 0; s < R; ++s) {
+                __builtin_amdgcn_sched_barrier(0);
+                load(ring[(s + R - 1) % R], min(b + (R - 1) * NW, last));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(ring[s], b);
+                b += NW;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < R - 1; ++s)
+            if (i + s < mine) compute(ring[s], b + s * NW);
     }
 
     // merge the waves: lane (j, g) holds query j, dims 16 c + 4 g + i
@@ -779,13 +859,12 @@ int64_t kv4_workspace_bytes(const Kv4Plan& p, int64_t B, int64_t H) {
 // tokens), where the 4-bit cache needs the 8 waves (31.6 against 27.7 us).
 template <bool kF16>
 hipError_t launch_attention_kernel(const Kv4Plan& p, const AttnArgs& a, hipStream_t stream) {
+    const dim3 grid(unsigned(p.grid));
     if constexpr (!kF16) {
         if (p.waves == 8)
-            return launch_kernel(kv4_attention_kernel<false, 8>, dim3(unsigned(p.grid)), dim3(512),
-                                 0, stream, a);
+            return launch_kernel(kv4_attention_kernel<false, 8>, grid, dim3(512), 0, stream, a);
     }
-    return launch_kernel(kv4_attention_kernel<kF16, 4>, dim3(unsigned(p.grid)), dim3(256), 0,
-                         stream, a);
+    return launch_kernel(kv4_attention_kernel<kF16, 4>, grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_kv4_attention(const Kv4Plan& p, const uint16_t* q, int64_t B, int64_t H,

@@ -221,6 +221,9 @@ hipError_t launch_w8a8_gemm(const VariantPlan& p, const int8_t* x8, const float*
 hipError_t launch_w4a4_gemm(const VariantPlan& p, const uint8_t* act, int64_t M, int64_t K,
                             const uint8_t* packed, int64_t N, uint16_t* y, hipStream_t stream);
 // KV4 decode attention (4-bit KV cache, SmoothAttention scaling)
+// Largest KV cache capacity (tokens per sequence) the entry points accept.
+constexpr int64_t kKv4MaxCapacity = int64_t(1) << 24;
+
 struct Kv4Plan {
     int splits;        // workgroups per (sequence, KV head), context split evenly
     int bps;           // 32-token blocks per split

@@ -200,6 +200,18 @@ def test_paired_schedule(B, H, Hkv, lens, C, paired, monkeypatch):
             assert np.all(got[b] == 0)
 
 
+@pytest.mark.parametrize("paired", ["1", "0"])
+def test_blocks_per_wave(paired, monkeypatch):
+    """Whole contexts per workgroup (one split), in the paired schedule's
+    8-wave workgroups and in 4-wave ones, on contexts of 0 to 48 blocks:
+    waves run none to several whole rounds of the block ring and end with
+    any number of blocks left in it, and the last block of a context is
+    full or partial."""
+    qoq.set_tuning("kv4_paired", paired)
+    _run(8, 8, 2, [0, 1, 100, 257, 500, 800, 1100, 1530], 1536, seed=41,
+         monkeypatch=monkeypatch, splits=1)
+
+
 def test_many_splits_merge(monkeypatch):
     """More than 16 splits of one context (one block each): the merge reads
     its splits in rounds of eight instead of all at once."""

@@ -297,84 +297,93 @@ constexpr int kPairMaxB = 256;
 // fp16 layout holds keys [tile 2][g 4][t 16][st 4][8 halves] and values
 // [g 4][d 16][c 8][8 halves] (tokens pi(8 g + e)), 8 KiB each.
 template <bool kF16, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kF16 ? 1 : 3)))
+__global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(kF16 ? 1 : (NW == 8 ? 2 : 3))))
 kv4_attention_kernel(AttnArgs a) {
     // blocks a wave holds in registers: the next block's loads are in flight
     // while one is computed (deeper rings, 3-5 blocks, measured slower on
     // every benchmarked batch: more registers, no latency left to hide)
     constexpr int R = 2;
+    // the 8-wave 4-bit workgroups run the paired schedule with both contexts
+    // in one stream of blocks: one merge slot per context
+    constexpr bool kPairStream = !kF16 && NW == 8;
+    constexpr int kSlots = kPairStream ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15;          // query of the group (MFMA column)
     const int g = lane >> 4;          // lane group
     const int64_t C = a.C;
-    __shared__ float sm[NW][16], sl[NW][16];
-    __shared__ float so[NW][16][kD + 4];
+    __shared__ float sm[kSlots][NW][16], sl[kSlots][NW][16];
+    __shared__ float so[kSlots][NW][16][kD + 4];
     __shared__ int rank_len[kPairMaxB], by_rank[kPairMaxB];
     auto clamped_len = [&](int b) { return int(min(int64_t(max(min(a.lens[b], a.max_len), 0)), C)); };
-
-  // one (sequence, KV head, split): the whole attention of its queries
-  auto run = [&](const int b_in, const int h, const int sp) {
-    // b comes from LDS in the paired schedule: the same in every lane
-    const int b = __builtin_amdgcn_readfirstlane(b_in);
-    const int region = b * a.Hkv + h;
-    const int len = __builtin_amdgcn_readfirstlane(clamped_len(b));
-    const int nb = (len + kBlk - 1) / kBlk;
-    const int blk0 = sp * a.bps;
-    const int blk1 = min(nb, blk0 + a.bps);
-    // a split past the end of its context writes nothing: the merge of the
-    // splits reads only those that hold tokens
-    if (a.splits > 1 && blk0 >= nb) return;
-    const uint8_t* rg = kF16 ? a.cache + int64_t(region) * C * (4 * kD)
-                             : a.cache + region_offset(region, C);
-    const uint8_t* kbase = rg;
-    const uint8_t* vbase = rg + (C / kBlk) * (kF16 ? 4 * kBlkBytes : kBlkBytes);
-    const uint8_t* mbase = rg + (C / kBlk) * 2 * kBlkBytes;
-    const bool qvalid = j < a.G;
-    const int qh = h * a.G + min(j, a.G - 1);
-
-    // smoothed query operand: lane (j, g), step st holds dims 32 st + 8 g + e
-    v8h qop[4];
-    float qsum = 0.0f;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int d0 = 32 * st + 8 * g;
-        const uint4 qq = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + qh) * kD + d0);
-        const uint4 ll = kF16 ? uint4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}
-                              : *reinterpret_cast<const uint4*>(a.lam + h * kD + d0);
-        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w}, lw[4] = {ll.x, ll.y, ll.z, ll.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const float x = h2f(uint16_t(qw[i] >> (16 * hf))) * h2f(uint16_t(lw[i] >> (16 * hf)));
-                const _Float16 xs = qvalid ? static_cast<_Float16>(x) : _Float16(0.0f);
-                qop[st][2 * i + hf] = xs;
-                qsum += float(xs);
-            }
-        }
-    }
-    qsum += __shfl_xor(qsum, 16, 64);
-    qsum += __shfl_xor(qsum, 32, 64);
     // scores in the log2 domain: log2(e) / sqrt(D)
     const float kScale = 1.4426950408889634f * 0.08838834764831845f;
+    const bool qvalid = j < a.G;
 
+    // state of the context being processed: its length, the smoothed query
+    // operand (lane (j, g), step st holds dims 32 st + 8 g + e) and the sum
+    // of its elements, the running maximum and sum, the output accumulators
+    int len = 0;
+    v8h qop[4];
+    float qsum = 0.0f;
     float m = -INFINITY, l = 0.0f;
     v4f o[8];
+
+    auto set_query = [&](int b, int h, v8h (&qo)[4], float& qs) {
+        const int qh = h * a.G + min(j, a.G - 1);
+        qs = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int st = 0; st < 4; ++st) {
+            const int d0 = 32 * st + 8 * g;
+            const uint4 qq = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + qh) * kD + d0);
+            const uint4 ll = kF16 ? uint4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}
+                                  : *reinterpret_cast<const uint4*>(a.lam + h * kD + d0);
+            const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w}, lw[4] = {ll.x, ll.y, ll.z, ll.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float x = h2f(uint16_t(qw[i] >> (16 * hf))) * h2f(uint16_t(lw[i] >> (16 * hf)));
+                    const _Float16 xs = qvalid ? static_cast<_Float16>(x) : _Float16(0.0f);
+                    qo[st][2 * i + hf] = xs;
+                    qs += float(xs);
+                }
+            }
+        }
+        qs += __shfl_xor(qs, 16, 64);
+        qs += __shfl_xor(qs, 32, 64);
+    };
+    auto reset = [&]() {
+        m = -INFINITY;
+        l = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    auto region_base = [&](int b, int h) {
+        const int region = b * a.Hkv + h;
+        return kF16 ? a.cache + int64_t(region) * C * (4 * kD) : a.cache + region_offset(region, C);
+    };
+    // 4-bit cache sections of a region as buffers (key and value codes at
+    // most 2^24 / 32 blocks x 2 KiB = 1 GiB each: 32-bit offsets)
+    struct Rs {
+        __amdgpu_buffer_rsrc_t k, v, m;
+    };
+    const int64_t nblk = C / kBlk;
+    auto region_rsrc = [&](int b, int h) {
+        const uint8_t* rg = region_base(b, h);
+        Rs rs;
+        rs.k = __builtin_amdgcn_make_buffer_rsrc((void*)rg, (short)0, int(nblk * kBlkBytes), 0x00020000);
+        rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(rg + nblk * kBlkBytes), (short)0,
+                                                 int(nblk * kBlkBytes), 0x00020000);
+        rs.m = __builtin_amdgcn_make_buffer_rsrc((void*)(rg + nblk * 2 * kBlkBytes), (short)0,
+                                                 int(nblk * kMetaBlkBytes), 0x00020000);
+        return rs;
+    };
 
     auto kofs = [&](int tile) { return (tile * 4 + g) * 256 + j * 16; };
     const int vofs = (g * 16 + j) * 32;
-    // 4-bit cache sections of the region as buffers (key and value codes at
-    // most 2^24 / 32 blocks x 2 KiB = 1 GiB each: 32-bit offsets)
-    const int64_t nblk = C / kBlk;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)kbase, (short)0, int(nblk * kBlkBytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)vbase, (short)0, int(nblk * kBlkBytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)mbase, (short)0, int(nblk * kMetaBlkBytes), 0x00020000);
     // per block: key codes (2 tiles), value codes, and the lane's 8 entries
     // of each metadata array (s_k, s_v, zero bytes); or the fp16 operands
     struct Blk4 {
@@ -384,11 +393,9 @@ kv4_attention_kernel(AttnArgs a) {
     struct Blk16 {
         uint4 k[8], v[8];
     };
-    using Blk = typename std::conditional<kF16, Blk16, Blk4>::type;
-    auto load = [&](auto& r, int blk) {
-      if constexpr (kF16) {
-        const uint8_t* kb = kbase + int64_t(blk) * 4 * kBlkBytes;
-        const uint8_t* vb = vbase + int64_t(blk) * 4 * kBlkBytes;
+    auto load16 = [&](Blk16& r, const uint8_t* rg, int blk) {
+        const uint8_t* kb = rg + int64_t(blk) * 4 * kBlkBytes;
+        const uint8_t* vb = rg + nblk * 4 * kBlkBytes + int64_t(blk) * 4 * kBlkBytes;
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
@@ -398,19 +405,19 @@ kv4_attention_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             r.v[c] = *reinterpret_cast<const uint4*>(vb + (g * 16 + j) * 128 + 16 * c);
-      } else {
-        // buffer loads: the lane offsets are fixed, the block offset is
-        // uniform (an SGPR), so no address arithmetic runs per block
+    };
+    // buffer loads: the lane offsets are fixed, the block offset is uniform
+    // (an SGPR), so no address arithmetic runs per block
+    auto load4 = [&](Blk4& r, const Rs& rs, int blk) {
         const int sb = blk * kBlkBytes;
-        const int sm = blk * kMetaBlkBytes;
-        r.k0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kofs(0), sb, 0));
-        r.k1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kofs(1), sb, 0));
-        r.v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs, sb, 0));
-        r.v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs + 16, sb, 0));
-        r.sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rm, 16 * g, sm, 0));
-        r.sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rm, 64 + 16 * g, sm, 0));
-        r.z = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rm, 128 + 8 * g, sm, 0));
-      }
+        const int smb = blk * kMetaBlkBytes;
+        r.k0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, kofs(0), sb, 0));
+        r.k1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, kofs(1), sb, 0));
+        r.v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, vofs, sb, 0));
+        r.v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, vofs + 16, sb, 0));
+        r.sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.m, 16 * g, smb, 0));
+        r.sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.m, 64 + 16 * g, smb, 0));
+        r.z = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.m, 128 + 8 * g, smb, 0));
     };
     const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
     // one code per 16-bit half; held in a VGPR so that mask-and-or fuses
@@ -549,44 +556,83 @@ kv4_attention_kernel(AttnArgs a) {
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), pv, o[c], 0, 0, 0);
         }
     };
-    auto compute = [&](const Blk& r, int blk) {
-        if constexpr (kF16) {
-            compute16(r, blk);
+
+    // a wave's state into merge slot `slot`: lane (j, g) holds query j,
+    // dims 16 c + 4 g + i
+    auto flush = [&](int slot) {
+        float lt = l;
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (g == 0) {
+            sm[slot][wave][j] = m;
+            sl[slot][wave][j] = lt;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[slot][wave][j][16 * c + 4 * g + i] = o[c][i];
+    };
+    // the waves' states of slot `slot` merged by 256 threads (thread t:
+    // query t / 16, 8 dims; G <= 16, so threads past the group hold no
+    // query): the output of sequence b, or the partial of split sp
+    auto merge = [&](int slot, int b, int h, int sp, int t) {
+        const int jq = t >> 4;
+        const int d0 = (t & 15) * 8;
+        if (jq >= a.G) return;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[slot][w][jq]);
+        float L = 0.0f, f[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            f[w] = M == -INFINITY ? 0.0f : exp2f(sm[slot][w][jq] - M);
+            L += f[w] * sl[slot][w][jq];
+        }
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[e] = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) acc[e] += f[w] * so[slot][w][jq][d0 + e];
+        }
+        const int64_t row = int64_t(b) * a.H + h * a.G + jq;
+        if (a.splits == 1) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = L > 0.0f ? acc[2 * e] / L : 0.0f;
+                const float x1 = L > 0.0f ? acc[2 * e + 1] / L : 0.0f;
+                pk[e] = uint32_t(__half_as_ushort(__float2half_rn(x0))) |
+                        (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+            }
+            *reinterpret_cast<uint4*>(a.out + row * kD + d0) = uint4{pk[0], pk[1], pk[2], pk[3]};
         } else {
-            compute4(r, blk);
+            float* pp = a.part + (row * a.splits + sp) * (kD + 4);
+            *reinterpret_cast<float4*>(pp + d0) = float4{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<float4*>(pp + d0 + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+            if (d0 == 0) {
+                pp[kD] = M;
+                pp[kD + 1] = L;
+            }
         }
     };
 
-    // the wave's blocks: blk0 + wave, + NW, ...; the loads of the next R - 1
-    // blocks are in flight while one is computed. Every step issues its load
-    // (block numbers past the wave's last block are clamped to it: cache
-    // hits, never used), so each compute waits for exactly its own block.
-    const int first = blk0 + wave;
-    if constexpr (kF16) {
-        // the fp16 cache (comparison point): two blocks, the next one's
-        // loads in flight while one is computed
-        Blk ra, rb;
-        int bi = first;
-        if (bi < blk1) load(ra, bi);
-        for (; bi < blk1; bi += 2 * NW) {
-            if (bi + NW < blk1) load(rb, bi + NW);
-            compute(ra, bi);
-            if (bi + NW >= blk1) break;
-            if (bi + 2 * NW < blk1) load(ra, bi + 2 * NW);
-            compute(rb, bi + NW);
-        }
-    } else if (first < blk1) {
-        // 4-bit cache: whole rounds of R blocks run unconditionally; the
-        // last R - 1 or fewer blocks are already in the ring when the rounds
-        // end and are only computed. Each block's loads stay together and in
-        // order (scheduling barriers), so the waits are the same in every
-        // round.
-        Blk ring[R];
-        const int last = blk1 - 1;
+    // The 4-bit block loop: this wave's blocks are the stream indices
+    // first, first + NW, ..., last (load_at / compute_at map an index to a
+    // context and block). The loads of the next R - 1 are in flight while
+    // one is computed; whole rounds of R blocks run unconditionally, and
+    // the last R - 1 or fewer blocks are already in the ring when the
+    // rounds end and are only computed. Every step issues its load (indices
+    // past the wave's last are clamped to it: cache hits, never used), and
+    // each block's loads stay together and in order (scheduling barriers),
+    // so each compute waits for exactly its own block.
+    auto block_loop = [&](int first, int last, auto load_at, auto compute_at) {
+        if (first > last) return;
+        Blk4 ring[R];
         const int mine = (last - first) / NW + 1;   // blocks of this wave
 #pragma unroll
         for (int s = 0; s < R - 1; ++s) {
-            load(ring[s], min(first + s * NW, last));
+            load_at(ring[s], min(first + s * NW, last));
             __builtin_amdgcn_sched_barrier(0);
         }
         int b = first, i = 0;
@@ -594,70 +640,102 @@ kv4_attention_kernel(AttnArgs a) {
 #pragma unroll
             for (int s = 0; s < R; ++s) {
                 __builtin_amdgcn_sched_barrier(0);
-                load(ring[(s + R - 1) % R], min(b + (R - 1) * NW, last));
+                load_at(ring[(s + R - 1) % R], min(b + (R - 1) * NW, last));
                 __builtin_amdgcn_sched_barrier(0);
-                compute(ring[s], b);
+                compute_at(ring[s], b);
                 b += NW;
             }
         }
 #pragma unroll
         for (int s = 0; s < R - 1; ++s)
-            if (i + s < mine) compute(ring[s], b + s * NW);
-    }
+            if (i + s < mine) compute_at(ring[s], b + s * NW);
+    };
 
-    // merge the waves: lane (j, g) holds query j, dims 16 c + 4 g + i
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (g == 0) {
-        sm[wave][j] = m;
-        sl[wave][j] = l;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) so[wave][j][16 * c + 4 * g + i] = o[c][i];
-    __syncthreads();
-    // thread -> (query jq, 8 dims); 16 queries x 128 dims over the first
-    // 256 threads (G <= 16: the others hold no query)
-    const int jq = threadIdx.x >> 4;
-    const int d0 = (threadIdx.x & 15) * 8;
-    if (jq >= a.G) return;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][jq]);
-    float L = 0.0f, f[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        f[w] = M == -INFINITY ? 0.0f : exp2f(sm[w][jq] - M);
-        L += f[w] * sl[w][jq];
-    }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        acc[e] = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) acc[e] += f[w] * so[w][jq][d0 + e];
-    }
-    const int64_t row = int64_t(b) * a.H + h * a.G + jq;
-    if (a.splits == 1) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x0 = L > 0.0f ? acc[2 * e] / L : 0.0f;
-            const float x1 = L > 0.0f ? acc[2 * e + 1] / L : 0.0f;
-            pk[e] = uint32_t(__half_as_ushort(__float2half_rn(x0))) |
-                    (uint32_t(__half_as_ushort(__float2half_rn(x1))) << 16);
+  // one (sequence, KV head, split): the whole attention of its queries
+  auto run = [&](const int b_in, const int h, const int sp) {
+    // b comes from LDS in the paired schedule: the same in every lane
+    const int b = __builtin_amdgcn_readfirstlane(b_in);
+    len = __builtin_amdgcn_readfirstlane(clamped_len(b));
+    const int nb = (len + kBlk - 1) / kBlk;
+    const int blk0 = sp * a.bps;
+    const int blk1 = min(nb, blk0 + a.bps);
+    // a split past the end of its context writes nothing: the merge of the
+    // splits reads only those that hold tokens
+    if (a.splits > 1 && blk0 >= nb) return;
+    set_query(b, h, qop, qsum);
+    reset();
+    const int first = blk0 + wave;
+    if constexpr (kF16) {
+        // the fp16 cache (comparison point): two blocks, the next one's
+        // loads in flight while one is computed
+        const uint8_t* rg = region_base(b, h);
+        Blk16 ra, rb;
+        int bi = first;
+        if (bi < blk1) load16(ra, rg, bi);
+        for (; bi < blk1; bi += 2 * NW) {
+            if (bi + NW < blk1) load16(rb, rg, bi + NW);
+            compute16(ra, bi);
+            if (bi + NW >= blk1) break;
+            if (bi + 2 * NW < blk1) load16(ra, rg, bi + 2 * NW);
+            compute16(rb, bi + NW);
         }
-        *reinterpret_cast<uint4*>(a.out + row * kD + d0) = uint4{pk[0], pk[1], pk[2], pk[3]};
     } else {
-        float* pp = a.part + (row * a.splits + sp) * (kD + 4);
-        *reinterpret_cast<float4*>(pp + d0) = float4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<float4*>(pp + d0 + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
-        if (d0 == 0) {
-            pp[kD] = M;
-            pp[kD + 1] = L;
-        }
+        const Rs rs = region_rsrc(b, h);
+        block_loop(first, blk1 - 1, [&](Blk4& r, int blk) { load4(r, rs, blk); },
+                   [&](const Blk4& r, int blk) { compute4(r, blk); });
     }
+    flush(0);
+    __syncthreads();
+    merge(0, b, h, sp, threadIdx.x);
+  };
+
+  // the paired schedule's two contexts (A, then B; bB == bA: A alone) as one
+  // stream of blocks over the workgroup's waves: a wave whose blocks cross
+  // from A to B parks its A state in slot 0 and goes on with B's query;
+  // both merges run at the end, on the two halves of the workgroup
+  auto run_pair = [&](const int bA_in, const int bB_in, const int h) {
+    const int bA = __builtin_amdgcn_readfirstlane(bA_in);
+    const int bB = __builtin_amdgcn_readfirstlane(bB_in);
+    const bool alone = bA == bB;
+    const int lenA = __builtin_amdgcn_readfirstlane(clamped_len(bA));
+    const int lenB = alone ? 0 : __builtin_amdgcn_readfirstlane(clamped_len(bB));
+    const int nA = (lenA + kBlk - 1) / kBlk;
+    const int nB = (lenB + kBlk - 1) / kBlk;
+    const Rs rsA = region_rsrc(bA, h);
+    const Rs rsB = region_rsrc(bB, h);
+    v8h qopB[4];
+    float qsumB;
+    set_query(bB, h, qopB, qsumB);
+    set_query(bA, h, qop, qsum);
+    len = lenA;
+    reset();
+    bool inB = false;
+    block_loop(
+        wave, nA + nB - 1,
+        [&](Blk4& r, int c) {
+            if (c < nA) load4(r, rsA, c);
+            else load4(r, rsB, c - nA);
+        },
+        [&](const Blk4& r, int c) {
+            if (c >= nA && !inB) {
+                flush(0);
+                reset();
+#pragma unroll
+                for (int st = 0; st < 4; ++st) qop[st] = qopB[st];
+                qsum = qsumB;
+                len = lenB;
+                inB = true;
+            }
+            compute4(r, inB ? c - nA : c);
+        });
+    if (!inB) {
+        flush(0);
+        reset();
+    }
+    flush(1);
+    __syncthreads();
+    if (threadIdx.x < 256) merge(0, bA, h, 0, threadIdx.x);
+    else if (!alone) merge(1, bB, h, 0, threadIdx.x - 256);
   };
 
     if (!a.paired) {
@@ -691,10 +769,14 @@ kv4_attention_kernel(AttnArgs a) {
     __syncthreads();
     const int p = blockIdx.x / a.Hkv;
     const int h = blockIdx.x % a.Hkv;
-    run(by_rank[p], h, 0);
-    if (a.B - 1 - p != p) {
-        __syncthreads();   // the merge buffers are reused
-        run(by_rank[a.B - 1 - p], h, 0);
+    if constexpr (kPairStream) {
+        run_pair(by_rank[p], by_rank[a.B - 1 - p], h);
+    } else {
+        run(by_rank[p], h, 0);
+        if (a.B - 1 - p != p) {
+            __syncthreads();   // the merge buffers are reused
+            run(by_rank[a.B - 1 - p], h, 0);
+        }
     }
 }
 

@@ -327,6 +327,7 @@ kv4_attention_kernel(AttnArgs a) {
     int len = 0;
     v8h qop[4];
     float qsum = 0.0f;
+    v8h qz;                           // query side of the zero-point MFMA
     float m = -INFINITY, l = 0.0f;
     v4f o[8];
 
@@ -353,6 +354,30 @@ kv4_attention_kernel(AttnArgs a) {
         }
         qs += __shfl_xor(qs, 16, 64);
         qs += __shfl_xor(qs, 32, 64);
+    };
+    // The key zero point enters the scores through a fifth MFMA per tile:
+    // its key side holds z_k 2^-17 in the lanes of the first k group
+    // (k = 0, 1, 2): the fp16 bit pattern z_k << 7 (patterns up to 0x7ff are
+    // linear in value, 2^-24 apart, so this is exact for z_k <= 15); its
+    // query side holds -sum(q~) 2^-7 there as three fp16 parts (their sum
+    // is the fp32 value but for the parts' 2^-24 resolution; 128 values of
+    // at most 65504 keep the largest part finite), so the MFMA adds
+    // -z_k sum(q~) 2^-24 to the 2^-24-scaled score.
+    auto make_qz = [&](float qs) {
+        const float x = qs * 0.0078125f;
+        const _Float16 p0 = static_cast<_Float16>(x);
+        const float r1 = x - float(p0);
+        const _Float16 p1 = static_cast<_Float16>(r1);
+        const _Float16 p2 = static_cast<_Float16>(r1 - float(p1));
+        v8h v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = _Float16(0.0f);
+        if (g == 0) {
+            v[0] = -p0;
+            v[1] = -p1;
+            v[2] = -p2;
+        }
+        return v;
     };
     auto reset = [&]() {
         m = -INFINITY;
@@ -388,7 +413,8 @@ kv4_attention_kernel(AttnArgs a) {
     // of each metadata array (s_k, s_v, zero bytes); or the fp16 operands
     struct Blk4 {
         uint4 k0, k1, v0, v1, sk, sv;
-        uint2 z;
+        uint2 z;      // zero bytes of the lane's output tokens
+        uint2 zr;     // zero bytes of the lane's key row tokens (j, 16 + j)
     };
     struct Blk16 {
         uint4 k[8], v[8];
@@ -418,7 +444,13 @@ kv4_attention_kernel(AttnArgs a) {
         r.sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.m, 16 * g, smb, 0));
         r.sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.m, 64 + 16 * g, smb, 0));
         r.z = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.m, 128 + 8 * g, smb, 0));
+        r.zr = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.m, 128 + 8 * (j >> 2), smb, 0));
     };
+    // byte j % 4 of the row word holds the zero of key row j (tile 0) and
+    // 16 + j (tile 1); only the first k group's lanes carry it
+    const uint32_t zsh = 8 * (j & 3);
+    const uint32_t zmask = g == 0 ? 0xfu : 0u;
+    const float kS24 = kScale * 16777216.0f;
     const uint32_t c64 = __builtin_amdgcn_readfirstlane(0x64646464u);
     // one code per 16-bit half; held in a VGPR so that mask-and-or fuses
     // into one v_and_or_b32 with the exponent constant in an SGPR
@@ -491,12 +523,13 @@ kv4_attention_kernel(AttnArgs a) {
             return tbase + tok < len;
         };
         const uint32_t skw[4] = {r.sk.x, r.sk.y, r.sk.z, r.sk.w};
-        // zero bytes z_k | z_v << 4 of the lane's tokens e = 0..3, 4..7
-        const uint32_t zk03 = r.z.x & 0x0f0f0f0fu, zk47 = r.z.y & 0x0f0f0f0fu;
+        // value zeros of the lane's tokens e = 0..3, 4..7 (zero bytes hold
+        // z_k | z_v << 4)
         const uint32_t zv03 = (r.z.x >> 4) & 0x0f0f0f0fu, zv47 = (r.z.y >> 4) & 0x0f0f0f0fu;
-        // scores: S[token, query] = q~ . u. The key codes enter the MFMA
-        // as the fp16 subnormals u * 2^-24 (their bit patterns, exact);
-        // products and sums are exact-scaled fp32, undone by the 2^24 below.
+        // scores: S[token, query] = q~ . (u - z_k). The key codes enter the
+        // MFMA as the fp16 subnormals u 2^-24 (their bit patterns, exact),
+        // the zero point through the fifth MFMA; the sum is 2^-24-scaled
+        // fp32, undone together with the scale s_k and log2(e) / sqrt(D).
         float zs[8];
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -509,13 +542,14 @@ kv4_attention_kernel(AttnArgs a) {
                 unpack_tiny(kw[st], nib, u);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(join(u), qop[st], acc, 0, 0, 0);
             }
+            const uint32_t zt = ((tile ? r.zr.y : r.zr.x) >> zsh) & zmask;
+            const uint4 zrow = uint4{zt * 0x00800080u, zt << 7, 0u, 0u};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, zrow), qz, acc, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * tile + i;
                 const h2 sk2 = __builtin_bit_cast(h2, skw[e >> 1]);
-                const float zk = float(((tile ? zk47 : zk03) >> (8 * i)) & 0xffu);
-                zs[e] = __builtin_fmaf(acc[i], 16777216.0f, -zk * qsum) *
-                        (float(sk2[e & 1]) * kScale);
+                zs[e] = acc[i] * (float(sk2[e & 1]) * kS24);
             }
         }
         uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
@@ -663,6 +697,7 @@ kv4_attention_kernel(AttnArgs a) {
     // splits reads only those that hold tokens
     if (a.splits > 1 && blk0 >= nb) return;
     set_query(b, h, qop, qsum);
+    qz = make_qz(qsum);
     reset();
     const int first = blk0 + wave;
     if constexpr (kF16) {
@@ -706,7 +741,9 @@ kv4_attention_kernel(AttnArgs a) {
     v8h qopB[4];
     float qsumB;
     set_query(bB, h, qopB, qsumB);
+    const v8h qzB = make_qz(qsumB);
     set_query(bA, h, qop, qsum);
+    qz = make_qz(qsum);
     len = lenA;
     reset();
     bool inB = false;
@@ -722,7 +759,7 @@ kv4_attention_kernel(AttnArgs a) {
                 reset();
 #pragma unroll
                 for (int st = 0; st < 4; ++st) qop[st] = qopB[st];
-                qsum = qsumB;
+                qz = qzB;
                 len = lenB;
                 inB = true;
             }

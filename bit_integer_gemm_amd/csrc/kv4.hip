@@ -778,12 +778,12 @@ kv4_attention_kernel(AttnArgs a) {
     if (!a.paired) {
         // 4-bit cache, split-major: the splits of one (sequence, KV head) are
         // `regions` ids apart, so with a multiple of 8 regions they all run
-        // on one XCD (ids are dealt to the XCDs round-robin) -- the one whose
-        // merge workgroup reads them back, region r's rows being merge
-        // workgroup r when G = 4 -- and the partials are still in that XCD's
-        // L2 (Llama-3-8B-shaped, 4 x 8-16K tokens: 22.6 -> 22.25 us). The
-        // fp16 cache keeps the splits of a region adjacent (split-major costs
-        // it 50.4 -> 51.2 us).
+        // on XCD region % 8 (ids are dealt to the XCDs round-robin), where the
+        // one-wave merge workgroups of that region's rows run too (merge
+        // workgroup i takes a row of a region r with r % 8 = i % 8), and the
+        // partials are still in that XCD's L2 (Llama-3-8B-shaped, 4 x 8-16K
+        // tokens: 22.6 -> 22.25 us). The fp16 cache keeps the splits of a
+        // region adjacent (split-major costs it 50.4 -> 51.2 us).
         const int regions = a.B * a.Hkv;
         const int region = kF16 ? blockIdx.x / a.splits : blockIdx.x % regions;
         const int sp = kF16 ? blockIdx.x % a.splits : blockIdx.x / regions;

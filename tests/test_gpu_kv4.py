@@ -235,6 +235,20 @@ def test_splits_of_ragged_contexts(B, H, Hkv, lens, C, splits, monkeypatch):
     _run(B, H, Hkv, lens, C, seed=37, monkeypatch=monkeypatch, splits=splits)
 
 
+@pytest.mark.parametrize("B,H,Hkv,lens,C,splits", [
+    (4, 4, 4, [300, 0, 1, 257], 320, 3),                       # G = 1
+    (2, 64, 4, [500, 33], 512, 5),                             # G = 16
+    (2, 8, 4, [1200, 0], 1216, 20),                            # more than 16 splits
+    (8, 8, 1, [0, 1, 31, 32, 33, 500, 1, 0], 512, 4),          # G = 8, empty and one-token
+])
+def test_splits_merged_on_the_regions_xcd(B, H, Hkv, lens, C, splits, monkeypatch):
+    """Split batches whose (sequence, KV head) regions come in whole rounds
+    of 8: the splits of a region and the one-wave merge workgroups of its
+    rows are numbered onto the same XCD."""
+    assert (B * Hkv) % 8 == 0
+    _run(B, H, Hkv, lens, C, seed=43, monkeypatch=monkeypatch, splits=splits)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
 def test_attention_every_split(splits, monkeypatch):
     _run(3, 8, 2, [300, 45, 257], 320, seed=17, monkeypatch=monkeypatch, splits=splits)

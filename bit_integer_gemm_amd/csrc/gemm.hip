@@ -1378,9 +1378,15 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
 }
 
 // Fused entry point: one launch of the fused family when M <= 8 and each
-// wave's K range fits kFusedGroups groups (K <= 8192 with 16 waves); other
-// shapes run the quantizer into the workspace, then the GEMM. (The fused
-// kernel takes up to 16 tokens when forced.)
+// wave's K range fits kFusedGroups groups (K <= 8192 with 16 waves), and for
+// 9-12 tokens on layers of at most 14336 columns with K = 4096-8192 (two
+// column blocks per workgroup past 4096 columns, halving the workgroups
+// that repeat the quantization: against the quantizer + GEMM launches, in
+// HIP graphs, K = 4096: N = 4096 7.6 -> 6.7-6.8 us, 6144 9.4 -> 8.5, 14336
+// 16.0 -> 12.4-12.6; K = 8192: N = 8192 15.8-16.0 -> 15.3-15.6, 10240
+// 26.1-26.3 -> 25.0-25.5; wider layers and 13 or more tokens stay faster
+// as two launches); other shapes run the quantizer into the workspace,
+// then the GEMM. (The fused kernel takes up to 16 tokens when forced.)
 // The "gemm" tuning value "fused,KW" forces the fused kernel with KW waves;
 // any other family forces the two-call path with that GEMM configuration.
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
@@ -1389,12 +1395,13 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     const int64_t ng = K / kGroup;
     const bool fits = M <= 16 && N * K / 2 < (int64_t(1) << 31) &&
                       M * K * 2 < (int64_t(1) << 31) && ng <= int64_t(kFusedGroups) * 16;
-    // by default only up to 8 tokens: beyond that the workgroups' repeated
-    // quantization costs more than the separate quantizer launch saves
-    const bool pays = M <= 8;
+    // beyond these the workgroups' repeated quantization costs more than
+    // the separate quantizer launch saves
+    const bool few = M > 8 && M <= 12 && N <= 14336 && K >= 4096 && K <= 8192;
+    const bool pays = M <= 8 || few;
     int kw = ng <= 4 * kFusedGroups ? 4 : (ng <= 8 * kFusedGroups ? 8 : 16);
     bool fused = fits && pays;
-    int fcb = 1;   // column blocks per fused workgroup
+    int fcb = few && N > 4096 ? 2 : 1;   // column blocks per fused workgroup
     const std::string tune = tuning(kTuneGemm);
     if (!tune.empty()) {
         const char* env = tune.c_str();

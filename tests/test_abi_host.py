@@ -285,11 +285,12 @@ def test_gemm_rejects_bad_arguments():
 
 
 def test_linear_workspace_bytes():
-    # one fused launch for M <= 8 and K <= 8192: no workspace
-    for M, K in [(1, 4096), (8, 8192), (8, 128)]:
+    # one fused launch for M <= 8 and K <= 8192, and for 9-12 tokens with
+    # K = 4096-8192 on this 4096-column layer: no workspace
+    for M, K in [(1, 4096), (8, 8192), (8, 128), (9, 4096), (12, 8192)]:
         assert qoq.qoq_linear_workspace_bytes(M, 4096, K) == 0
     # otherwise x8 (tile layout) + token scales, each 256-byte aligned
-    for M, K in [(9, 4096), (16, 128), (64, 4096), (8, 14336), (4096, 4096)]:
+    for M, K in [(9, 2048), (13, 4096), (16, 128), (64, 4096), (8, 14336), (4096, 4096)]:
         act = qoq.qoq_act_bytes(M, K)
         want = -(-act // 256) * 256 + -(-4 * M // 256) * 256
         assert qoq.qoq_linear_workspace_bytes(M, 4096, K) == want
@@ -300,7 +301,10 @@ def test_linear_workspace_bytes():
 def test_linear_path(monkeypatch):
     qoq.set_tuning("gemm", None)
     # one fused launch for M <= 8 with K <= 8192, otherwise two launches
-    assert [qoq.qoq_linear_path(M, 4096, 4096) for M in (1, 8, 9, 64, 256)] == [1, 1, 0, 0, 0]
+    assert [qoq.qoq_linear_path(M, 4096, 4096) for M in (1, 8, 9, 12, 13, 64, 256)] == [1, 1, 1, 1, 0, 0, 0]
+    # 9-12 tokens fuse on layers up to 14336 columns with K = 4096-8192 only
+    assert [qoq.qoq_linear_path(10, N, 4096) for N in (6144, 14336, 14352, 28672)] == [1, 1, 0, 0]
+    assert [qoq.qoq_linear_path(10, 8192, K) for K in (2048, 4096, 8192)] == [0, 1, 1]
     assert qoq.qoq_linear_path(8, 4096, 16384) == 0
     assert qoq.qoq_linear_path(0, 4096, 4096) == -1 and qoq.qoq_linear_path(4, 4008, 4096) == -1
     qoq.set_tuning("gemm", "fused,16")

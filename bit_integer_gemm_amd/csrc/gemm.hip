@@ -1377,16 +1377,27 @@ hipError_t launch_gemm(const GemmPlan& p, const int8_t* x8, const float* s_x, in
     }
 }
 
-// Fused entry point: one launch of the fused family when M <= 8 and each
-// wave's K range fits kFusedGroups groups (K <= 8192 with 16 waves), and for
-// 9-12 tokens on layers of at most 14336 columns with K = 4096-8192 (two
-// column blocks per workgroup past 4096 columns, halving the workgroups
-// that repeat the quantization: against the quantizer + GEMM launches, in
-// HIP graphs, K = 4096: N = 4096 7.6 -> 6.7-6.8 us, 6144 9.4 -> 8.5, 14336
-// 16.0 -> 12.4-12.6; K = 8192: N = 8192 15.8-16.0 -> 15.3-15.6, 10240
-// 26.1-26.3 -> 25.0-25.5; wider layers and 13 or more tokens stay faster
-// as two launches); other shapes run the quantizer into the workspace,
-// then the GEMM. (The fused kernel takes up to 16 tokens when forced.)
+// Fused entry point: one launch of the fused family (each wave's K range
+// must fit kFusedGroups groups: K <= 8192 with 16 waves) when the repeated
+// quantization stays small against the quantizer launch it saves. Every
+// workgroup of one column block quantizes all M x K activations, so the
+// launch quantizes R = M K ceil(N / 16) values in all:
+//   * up to 12 tokens (9-12 only for K >= 4096): fused while R <= 64e6;
+//     otherwise two launches;
+//   * one column block per workgroup up to 4 tokens; from 5 tokens two
+//     (half the workgroups, half of R) once R > 16e6 or, past 8 tokens,
+//     N > 4096.
+// Measured in HIP graphs against the quantizer + GEMM launches (us, fused /
+// two launches): K = 4096, N = 4096: M = 8 5.9 / 7.3, M = 12 6.8 / 7.6;
+// N = 6144, M = 9-12: 8.5 / 9.4 (two blocks); N = 14336: M = 8 11.0 / 15.8,
+// M = 12 12.7 / 15.9 (two blocks); N = 28672: M = 8 17.7 / 18.3 (two
+// blocks), M = 9-12 two launches (18.3 against 19.5-19.9); K = 8192:
+// N = 8192 and 10240, M = 9-12 15.3 / 15.9 and 25.4 / 26.2 (two blocks);
+// N = 24576, M = 4 26.9 / 30.9 but M = 8 two launches (30.3 against 36.5 with
+// two blocks, 48.7 with one); N = 49152, M = 4 and 8 two launches (48.4
+// against 52.1, 48.6 against 68-92). Other shapes run the quantizer into the
+// workspace, then the GEMM.
+// (The fused kernel takes up to 16 tokens when forced.)
 // The "gemm" tuning value "fused,KW" forces the fused kernel with KW waves;
 // any other family forces the two-call path with that GEMM configuration.
 LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
@@ -1395,13 +1406,13 @@ LinearPlan plan_linear(int64_t M, int64_t N, int64_t K) {
     const int64_t ng = K / kGroup;
     const bool fits = M <= 16 && N * K / 2 < (int64_t(1) << 31) &&
                       M * K * 2 < (int64_t(1) << 31) && ng <= int64_t(kFusedGroups) * 16;
-    // beyond these the workgroups' repeated quantization costs more than
-    // the separate quantizer launch saves
-    const bool few = M > 8 && M <= 12 && N <= 14336 && K >= 4096 && K <= 8192;
-    const bool pays = M <= 8 || few;
+    // values quantized over all workgroups (only up to 16 tokens matter)
+    const int64_t quantized = M <= 16 ? M * K * ((N + kBlockCols - 1) / kBlockCols) : 0;
+    const bool pays = M <= 12 && (M <= 8 || K >= 4096) && quantized <= 64000000;
     int kw = ng <= 4 * kFusedGroups ? 4 : (ng <= 8 * kFusedGroups ? 8 : 16);
     bool fused = fits && pays;
-    int fcb = few && N > 4096 ? 2 : 1;   // column blocks per fused workgroup
+    // column blocks per fused workgroup
+    int fcb = M > 4 && (quantized > 16000000 || (M > 8 && N > 4096)) ? 2 : 1;
     const std::string tune = tuning(kTuneGemm);
     if (!tune.empty()) {
         const char* env = tune.c_str();

@@ -285,8 +285,8 @@ def test_gemm_rejects_bad_arguments():
 
 
 def test_linear_workspace_bytes():
-    # one fused launch for M <= 8 and K <= 8192, and for 9-12 tokens with
-    # K = 4096-8192 on this 4096-column layer: no workspace
+    # one fused launch (up to 12 tokens, K <= 8192, little repeated
+    # quantization on this 4096-column layer): no workspace
     for M, K in [(1, 4096), (8, 8192), (8, 128), (9, 4096), (12, 8192)]:
         assert qoq.qoq_linear_workspace_bytes(M, 4096, K) == 0
     # otherwise x8 (tile layout) + token scales, each 256-byte aligned
@@ -302,8 +302,13 @@ def test_linear_path(monkeypatch):
     qoq.set_tuning("gemm", None)
     # one fused launch for M <= 8 with K <= 8192, otherwise two launches
     assert [qoq.qoq_linear_path(M, 4096, 4096) for M in (1, 8, 9, 12, 13, 64, 256)] == [1, 1, 1, 1, 0, 0, 0]
-    # 9-12 tokens fuse on layers up to 14336 columns with K = 4096-8192 only
-    assert [qoq.qoq_linear_path(10, N, 4096) for N in (6144, 14336, 14352, 28672)] == [1, 1, 0, 0]
+    # up to 12 tokens fused while M K ceil(N / 16) <= 64e6 (9-12 tokens only
+    # for K >= 4096)
+    assert [qoq.qoq_linear_path(1, N, 8192) for N in (24576, 49152)] == [1, 1]
+    assert [qoq.qoq_linear_path(4, N, 8192) for N in (24576, 49152)] == [1, 0]
+    assert [qoq.qoq_linear_path(8, N, 8192) for N in (8192, 15616, 15632, 24576, 49152)] == [1, 1, 0, 0, 0]
+    assert [qoq.qoq_linear_path(8, N, 4096) for N in (14336, 28672)] == [1, 1]
+    assert [qoq.qoq_linear_path(10, N, 4096) for N in (6144, 14336, 24992, 25008, 28672)] == [1, 1, 1, 0, 0]
     assert [qoq.qoq_linear_path(10, 8192, K) for K in (2048, 4096, 8192)] == [0, 1, 1]
     assert qoq.qoq_linear_path(8, 4096, 16384) == 0
     assert qoq.qoq_linear_path(0, 4096, 4096) == -1 and qoq.qoq_linear_path(4, 4008, 4096) == -1

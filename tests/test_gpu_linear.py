@@ -22,10 +22,12 @@ DEV = "cuda:0"
 # waves, column counts that fill no tile
 FUSED = [(1, 128, 16), (1, 4096, 4096), (5, 640, 208), (8, 1152, 400), (8, 8192, 528),
          (3, 2048, 1040), (4, 512, 512), (2, 384, 48),
-         # 9-12 tokens: one column block per workgroup up to 4096 columns,
-         # two beyond (an odd block count: the last workgroup's second block
-         # lies past N), 8 or 16 waves
-         (9, 4096, 4096), (10, 4096, 6144), (11, 4096, 4112), (12, 8192, 1040)]
+         # 5-12 tokens with two column blocks per workgroup (more than 16e6
+         # values quantized, or 9-12 tokens past 4096 columns; odd block
+         # counts: the last workgroup's second block lies past N), 8 or 16
+         # waves; 9 tokens on 4096 columns with one block
+         (8, 4096, 8208), (6, 8192, 5648), (9, 4096, 4096), (10, 4096, 6144),
+         (11, 4096, 4112), (12, 8192, 1040)]
 # (the fused kernel also takes up to 16 tokens when forced)
 FORCED = FUSED + [(16, 8192, 528), (13, 2048, 1040), (9, 512, 512), (12, 640, 16)]
 TWO_CALL = [(17, 1024, 208), (64, 4096, 4096), (8, 14336, 272), (100, 640, 400), (16, 512, 512)]

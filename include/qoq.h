@@ -210,7 +210,7 @@ qoq_status qoq_w4a8_gemm_noalloc(const int8_t* x8, const float* s_x, int64_t M, 
                                  void* stream);
 
 /* Workspace bytes qoq_w4a8_linear needs for this shape: 0 when it runs as
- * one fused launch (M <= 8 and K <= 8192), otherwise room for the x8 codes,
+ * one fused launch (see qoq_w4a8_linear), otherwise room for the x8 codes,
  * the token scales and the GEMM's own workspace. No zero-fill is needed.
  * Host-only. */
 size_t qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -222,9 +222,11 @@ int qoq_linear_path(int64_t M, int64_t N, int64_t K);
 
 /* Per-token activation quantization and W4A8 GEMM in one call (run time).
  * Same result as qoq_quantize_act followed by qoq_w4a8_gemm, bit for bit
- * (codes, accumulators and y). For M <= 8 and K <= 8192 a single kernel
- * does both: every workgroup quantizes the few tokens itself, which removes
- * a launch of almost no work from the decode step (pages: velog notes on
+ * (codes, accumulators and y). For up to 12 tokens (9-12 only when
+ * K >= 4096) with K <= 8192 and M * K * ceil(N / 16) <= 64e6 (the values the
+ * workgroups quantize in all) a single kernel does both: every workgroup
+ * quantizes the few tokens itself, which removes a launch of almost no work
+ * from the decode step (pages: velog notes on
  * QServe, "Methods / 2) System: QServe", and "Part5 LLM部署技术" section 3,
  * on fusing the CUDA-core work into the GEMM). Other shapes run the
  * quantizer into `workspace`, then the GEMM.

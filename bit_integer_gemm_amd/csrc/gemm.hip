@@ -1179,41 +1179,52 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         // over K, about one workgroup of 8 waves per CU
         p.kind = 2; p.cb = 1; p.kw = 8; p.pd = 4;
         p.splits = int(std::min<int64_t>(std::max<int64_t>(256 / ((nbt + 7) / 8), 1), ng / 32));
-    } else if (M > 32 && M <= 64 && nbt >= 1152 && nbt <= 1920 && ng >= 32) {
-        // 33-64 tokens on layers of 18432-30720 columns (Qwen1.5-72B qkv at
-        // M = 64): K-split 32x32 family, 64 x 96 tiles (about one per CU),
-        // 4 waves splitting K, rings of 3 groups (31.3-31.7 -> 27.1 us
-        // against the shared-activation family with K in two ranges)
+    } else if (M > 32 && M <= 64 && nbt >= 1152 && nbt <= 1920 && ng >= 64) {
+        // 33-64 tokens on layers of 18432-30720 columns and K >= 8192
+        // (Qwen1.5-72B qkv at M = 64): K-split 32x32 family, 64 x 96 tiles
+        // (about one per CU), 4 waves splitting K, rings of 3 groups
+        // (31.3-31.7 -> 27.1 us against the shared-activation family with K
+        // in two ranges); with K = 4096 the shared-activation family is
+        // faster (Llama-3-8B gate+up at M = 48: 26.5 -> 18.7 us)
         p.kind = 5; p.mt = 2; p.cb = 3; p.kw = 4; p.pd = 3;
+    } else if (M > 8 && M <= 16 && nbt >= 1152 && nbt <= 1920 && ng >= 64) {
+        // 9-16 tokens on the same layers: K-split 32x32 family, 32 x 96
+        // tiles, 8 waves splitting K (Qwen1.5-72B qkv at M = 16: 27.6 ->
+        // 22.0 us against the shared-activation family)
+        p.kind = 5; p.mt = 1; p.cb = 3; p.kw = 8; p.pd = 2;
     } else if (M <= 64 && nbt <= 512) {
         p.kind = 1;
-        if (p.mt == 1) { p.cb = 1; p.kw = 8; p.pd = 4; }
+        // up to 16 tokens, two 16-column blocks per workgroup once that
+        // still gives 256 workgroups (Qwen1.5-72B down at M = 16: 27.4 ->
+        // 22.6 us; Llama-3-8B down, 256 blocks, keeps one: 9.9 against 12.4)
+        if (p.mt == 1) { p.cb = nbt >= 512 ? 2 : 1; p.kw = 8; p.pd = 4; }
         else if (p.mt == 2) { p.cb = 1; p.kw = 8; p.pd = 4; }
         else if (nbt >= 512) { p.cb = 2; p.kw = 4; p.pd = 2; }
         else if (nbt % 16 == 0) { p.mt = 2; p.cb = 2; p.kw = 8; p.pd = 4; }   // two row tiles
         else { p.cb = 1; p.kw = 8; p.pd = 4; }
         while (p.kw > 2 && ng < 2 * p.kw) p.kw /= 2;
         if (!decode_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.cb = 1; p.kw = 8; p.pd = 2; }
-    } else if (M > 128 && M <= 256 && nbt <= 512) {
+    } else if ((M > 128 && M <= 256 && nbt <= 512) ||
+               (M > 64 && M <= 128 && nbt <= 512 && ng <= 32)) {
         // narrow layers at 129-256 tokens (Llama-3-8B qkv / o / down at
         // M = 256): K-split 32x32 family, 64-row tiles of 64 or 96 columns
         // (whichever is closer to one workgroup per CU), 4 waves splitting
         // K, rings of 3 groups (o 12.8 -> 10.5 us, qkv 16.9 -> 13.2 us,
-        // down 32.0 -> 26.5 us against the previous rules)
+        // down 32.0 -> 26.5 us against the previous rules); at 65-128
+        // tokens only for short K (Llama-3-8B o / qkv at M = 96: 12.0 ->
+        // 9.9 us, 14.9 -> 10.0 us; down keeps the rules below: 21.5 against
+        // 23.9 us)
         p.kind = 5; p.mt = 2; p.kw = 4; p.pd = 3;
         const int64_t rows = (M + 63) / 64;
         p.cb = rows * ((nbt + 3) / 4) > 256 && rows * ((nbt + 5) / 6) >= 192 ? 3 : 2;
-    } else if (M > 64 && M <= 256 && nbt <= 256 && ng <= 32 && nbt % 16 == 0) {
-        // short, narrow layers at a few hundred tokens (Llama-3-8B o at
-        // M = 256): the decode family's K-split waves over 64-row tiles beat
-        // the 32x32 tiles, which leave half the CUs with one wave per SIMD;
-        // 64 channels per workgroup once that still gives 256 workgroups
-        // (o at M = 256: 14.3 -> 13.1 us against 32 channels)
-        p.kind = 1; p.mt = 4; p.cb = nbt >= 256 ? 4 : 2; p.kw = 4; p.pd = 2;
     } else if (M <= 64) {
         p.kind = 2;
         p.cb = 1;
-        if (nbt >= 2048) { p.kw = 12; p.pd = 2; }   // waves per workgroup, ring depth
+        // waves per workgroup, ring depth; up to 16 tokens on the widest
+        // layers two 16-column blocks per wave (Qwen1.5-72B gate+up at
+        // M = 16: 45.6 -> 40.1 us against 12 waves of one)
+        if (nbt >= 2048 && p.mt == 1) { p.cb = 2; p.kw = 8; p.pd = 2; }
+        else if (nbt >= 2048) { p.kw = 12; p.pd = 2; }
         else if (p.mt == 4 && ng >= 64) { p.kw = 16; p.pd = 2; p.splits = 2; }
         else { p.kw = 8; p.pd = 4; }
         if (!lds_config_exists(p.mt, p.cb, p.kw, p.pd)) { p.kw = 8; p.pd = 2; p.splits = 1; }
@@ -1224,9 +1235,27 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         const int64_t rows128 = (M + 127) / 128;
         const int64_t t42 = rows128 * ((nbt + 15) / 16);       // 128 x 256 tiles
         const int64_t t22 = ((M + 63) / 64) * ((nbt + 15) / 16);
-        // whole rounds of one 256 x 256 tile per CU: the tail round is >= 90 % full
+        // A 256 x 256 tile (one per CU) takes about the time of two 128 x 256
+        // tiles: the wide tiles when their rounds over the CUs take no more
+        // of that time than the 128 x 256 tiles' rounds (past 128 tokens).
+        // Measured (us, wide / 32x32-family tiles): Llama-3-8B gate+up at
+        // M = 512 60.3 / 77.9, qkv at M = 2048 54.1 / 66.3; Qwen1.5-72B
+        // gate+up at M = 192 105.7 / 123.4, qkv at M = 512 99.9 / 114.0 and
+        // M = 2048 337.8 / 342.0, down at M = 2048 320.7 / 364.4; fewer tiles
+        // than that stay on the 32x32 family (Llama-3-8B o and down at
+        // M = 2048: 47.6-48.3 / 38.8, 132.8 / 114.6).
+        // Deep, narrow layers with fewer tiles than CUs keep K in two ranges
+        // (the rule below; Qwen1.5-72B down at M = 1024, 128 tiles: 182 us
+        // against 192-197 in one).
         const int64_t t256 = ((M + 255) / 256) * ((nbt + 15) / 16);
-        const bool wide_fills = t256 >= 512 && (t256 % 256 == 0 || t256 % 256 >= 230);
+        auto rounds = [](int64_t t) { return (t + 255) / 256; };
+        const bool deep_narrow = M >= 512 && N <= 8192 && t42 >= 256 && ng >= 128;
+        // (only where 256-row tiles pad M no further than 128-row ones: at
+        // M = 320 and 384 they lose, qkv 78.1 -> 101.5 us, gate+up 56.5 ->
+        // 61.7 and 60.0 -> 63.0 us)
+        const bool same_rows = M % 256 == 0 || M % 256 > 128;
+        const bool wide_fills = M > 128 && same_rows && 2 * rounds(t256) <= rounds(t42) &&
+                                !(deep_narrow && t256 < 256);
         if (wide_fills) {
             // wide-tile family: 256 x 256 tiles of 8 waves, activations
             // staged by direct LDS loads three groups deep (Qwen1.5-72B
@@ -1234,7 +1263,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
             // tiles of the 32x32 family)
             p.kind = 6; p.mt = 8; p.cb = 1; p.nw = 8; p.pd = 3; p.pa = 1;
         }
-        else if (M >= 512 && N <= 8192 && t42 >= 256 && ng >= 128) {
+        else if (deep_narrow) {
             // deep and narrow: wide-tile family, 256 x 256 tiles, K in two
             // ranges (Qwen1.5-72B down at M = 1024: 192-197 -> 182 us)
             p.kind = 6; p.mt = 8; p.cb = 1; p.nw = 8; p.pd = 3; p.pa = 1; p.splits = 2;
@@ -1254,10 +1283,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
             p.mt = 1; p.cb = 1; p.pd = 4; p.pa = 3;   // 32 x 128 tiles: twice the workgroups
         }
         else { p.mt = 2; p.cb = 1; p.pd = 4; }
-        // under one workgroup per CU and a long K: split K to about two per CU
+        // 32x32-family tiles under one workgroup per CU and a long K: split K
+        // to about two per CU (the wide tiles split only by the rule above)
         const int64_t tiles = ((M + 32 * p.mt - 1) / (32 * p.mt)) *
                               ((nbt + 2 * p.cb * p.nw - 1) / (2 * p.cb * p.nw));
-        if (tiles < 256 && ng >= 64 && p.splits == 1)
+        if (p.kind == 4 && tiles < 256 && ng >= 64 && p.splits == 1)
             p.splits = int(std::min<int64_t>((512 + tiles - 1) / tiles, ng / 16));
     }
     const std::string tune = tuning(kTuneGemm);

@@ -63,7 +63,7 @@ int main() {
            QOQ_ERR_NULL);
     EXPECT(qoq_w4a8_gemm(p8, pf, 64, 16384, P, p16, 4096, 128, p16, nullptr, nullptr, 0, nullptr),
            QOQ_ERR_WORKSPACE);
-    EXPECT(qoq_w4a8_gemm_noalloc(p8, pf, 2048, 24576, P, p16, 8192, 128, p16, nullptr, nullptr),
+    EXPECT(qoq_w4a8_gemm_noalloc(p8, pf, 1280, 24576, P, p16, 8192, 128, p16, nullptr, nullptr),
            QOQ_ERR_WORKSPACE);
     EXPECT(qoq_w4a8_linear(p16, 64, 4096, P, p16, 4096, 128, p16, nullptr, nullptr, 0, nullptr),
            QOQ_ERR_WORKSPACE);

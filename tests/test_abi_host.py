@@ -284,6 +284,14 @@ def test_gemm_rejects_bad_arguments():
         assert call(M=M, workspace=P + 4, workspace_bytes=need) == ALIGN
 
 
+def test_deep_narrow_layers_split_k_below_a_round_of_wide_tiles():
+    # Qwen1.5-72B down (K = 24576, N = 8192): K in two ranges while its
+    # 256 x 256 tiles are fewer than the CUs (M = 1024: 128 tiles, 1280: 160),
+    # one range from a full round (M = 2048: 256 tiles)
+    ws = [qoq.qoq_gemm_workspace_bytes(M, 8192, 24576) for M in (1024, 1280, 2048)]
+    assert ws == [2 * 1024 * 8192 * 4, 2 * 1280 * 8192 * 4, 0]
+
+
 def test_linear_workspace_bytes():
     # one fused launch (up to 12 tokens, K <= 8192, little repeated
     # quantization on this 4096-column layer): no workspace

@@ -121,11 +121,38 @@ def test_decode_family_row_tiles(monkeypatch, cfg):
             _run(monkeypatch, _fmt("decode", cfg), M, 1152, N)
 
 
-@pytest.mark.parametrize("M,K,N", [(65, 256, 512), (128, 1152, 4096), (100, 4096, 256)])
-def test_decode_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
-    """Short, narrow layers at 65-128 tokens take the decode family by
-    default (64-row tiles paired 8 workgroup ids apart), including fewer
-    groups than waves."""
+def _default_plan(M, K, N):
+    """The default plan for a shape: accumulators bit-exact, y within the
+    tolerance."""
+    qoq.set_tuning("gemm", None)
+    pw, x8, s_x, ref = _case(M, K, N)
+    print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
+    y, acc = qoq.w4a8_gemm(x8, s_x, pw, acc_debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    yy = y.cpu().numpy().astype(np.float64)
+    err = np.abs(yy - ref["y"]) / np.maximum(np.abs(ref["y"]), 2.0 ** -14)
+    assert err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 1024, 8192), (5, 2048, 8192), (16, 1024, 32768),
+                                   (3, 1024, 33024), (12, 8192, 18432)])
+def test_plans_for_up_to_16_tokens_on_wide_layers(M, K, N, monkeypatch):
+    """Up to 16 tokens: the decode family with two 16-column blocks per
+    workgroup on 512-block layers (N = 8192), the shared-activation family
+    with two blocks per wave on layers of 2048 blocks or more (N = 33024: an
+    odd block count, the last wave's second block outside), and for 9-16
+    tokens on 18432-30720-column layers with K >= 8192 the K-split family's
+    32 x 96 tiles."""
+    _default_plan(M, K, N)
+
+
+@pytest.mark.parametrize("M,K,N", [(65, 256, 512), (128, 1152, 4096), (100, 4096, 256),
+                                   (96, 4096, 6144)])
+def test_ksplit_plan_for_65_to_128_tokens(M, K, N, monkeypatch):
+    """Narrow layers with short K (at most 32 groups) at 65-128 tokens take
+    the K-split 32x32 family's 64 x 64 tiles by default, including fewer
+    groups than waves and a ragged second row tile."""
     qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
@@ -156,11 +183,11 @@ def test_ksplit_plan_for_a_few_hundred_tokens(M, K, N, monkeypatch):
     assert err.max() <= 2e-3
 
 
-@pytest.mark.parametrize("M,K,N", [(40, 4096, 18432), (64, 5120, 30720)])
+@pytest.mark.parametrize("M,K,N", [(40, 8192, 18432), (48, 4096, 18432)])
 def test_ksplit_plan_for_wide_layers_at_64_tokens(M, K, N, monkeypatch):
-    """33-64 tokens on layers of 18432-30720 columns with K >= 4096 take the
-    K-split family's 64 x 96 tiles by default (M = 40: rows 40-63 of the
-    tile padded; K = 5120: 40 groups, 10 per wave)."""
+    """33-64 tokens on layers of 18432-30720 columns take the K-split
+    family's 64 x 96 tiles by default when K >= 8192 (M = 40: rows 40-63 of
+    the tile padded), the shared-activation family when K = 4096."""
     qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)
@@ -172,11 +199,12 @@ def test_ksplit_plan_for_wide_layers_at_64_tokens(M, K, N, monkeypatch):
     assert err.max() <= 2e-3
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 256, 65536)])
+@pytest.mark.parametrize("M,K,N", [(192, 256, 36864), (200, 256, 36864), (512, 256, 32768)])
 def test_wide_tile_plan_when_tiles_fill_rounds(M, K, N, monkeypatch):
-    """Shapes whose 256 x 256 tiles fill whole rounds of the CUs (here 2 x 256
-    tiles, the second row tile ragged at 44 rows) take the wide-tile family
-    by default."""
+    """Past 128 tokens, shapes whose 256 x 256 tiles need no more rounds of
+    the CUs than twice the 128 x 256 tiles' (and pad the rows no further)
+    take the wide-tile family by default: 144 tiles at M = 192 and 200 (rows
+    padded to 256), 256 tiles at M = 512."""
     qoq.set_tuning("gemm", None)
     pw, x8, s_x, ref = _case(M, K, N)
     print(f"\n[gpu-case] default plan M={M} K={K} N={N}", flush=True)

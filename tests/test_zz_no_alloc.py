@@ -65,7 +65,7 @@ def test_noalloc_matches_workspace_path(pair):
 def test_noalloc_refuses_oversized_split():
     """A shape whose split-K partial sums exceed the scratch array is
     refused before anything is launched (no buffer is touched)."""
-    M, K, N = 2048, 24576, 8192
+    M, K, N = 1280, 24576, 8192
     assert qoq.qoq_gemm_workspace_bytes(M, N, K) > qoq.NOALLOC_SCRATCH_BYTES
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the call refuses first
     st = qoq.qoq_w4a8_gemm_noalloc(fake, fake, M, K, fake, fake, N, 128, fake, None, None)

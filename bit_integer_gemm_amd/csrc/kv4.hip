@@ -920,13 +920,18 @@ int64_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t C) { return B * Hkv * C 
 // per-workgroup query set-up and merge cost more than the imbalance.)
 // The "kv4_splits" tuning key forces n splits. Unsplit batches of 2..256
 // sequences whose pairs fit one per CU take the paired schedule (8-wave
-// workgroups); the "kv4_paired" key set to "0" turns it off.
+// workgroups) when the longest context has 1024 tokens or more; the
+// "kv4_paired" key set to "0" turns it off, set to "1" takes it whenever the
+// batch allows it.
 Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     Kv4Plan p{};
     const int64_t nb = std::max<int64_t>(1, (max_len + kBlk - 1) / kBlk);
     const int64_t regions = std::max<int64_t>(1, B * Hkv);
     int64_t splits = (512 + regions - 1) / regions;
-    splits = std::max<int64_t>(1, std::min<int64_t>(splits, (nb + 3) / 4));
+    // at most 32: the merge reads more than 16 splits in several rounds
+    // (one context of 16K / 64K tokens on 8 KV heads: 64 splits 13.9 / 25.3
+    // us, 32 splits 11.5 / 21.7 us)
+    splits = std::max<int64_t>(1, std::min<int64_t>({splits, (nb + 3) / 4, int64_t(32)}));
     const std::string tune_splits = tuning(kTuneKv4Splits);
     if (!tune_splits.empty()) {
         const int v = std::atoi(tune_splits.c_str());
@@ -939,8 +944,15 @@ Kv4Plan plan_kv4(int64_t B, int64_t Hkv, int64_t max_len) {
     // pairs as 8-wave workgroups, at most one per CU (more pairs than CUs
     // would run two contexts back to back per 4-wave workgroup, which costs
     // the fp16 cache more than it saves: 121 -> 133 us on 16 x 64 heads)
-    p.paired = splits == 1 && B >= 2 && B <= kPairMaxB && (B + 1) / 2 * Hkv <= 256;
-    if (tuning(kTuneKv4Paired) == "0") p.paired = false;
+    // pairs only for contexts of 1024 tokens or more: the 8-wave pair
+    // workgroups run one per CU, and short contexts gain more from the
+    // 4-wave workgroups three to a CU (64 sequences of 128-512 tokens: 11.8
+    // -> 9.6 us unpaired; of 512-2048: 21.8-22.2 paired, 22.4-22.9 not)
+    const bool can_pair = splits == 1 && B >= 2 && B <= kPairMaxB && (B + 1) / 2 * Hkv <= 256;
+    p.paired = can_pair && max_len >= 1024;
+    const std::string tune_paired = tuning(kTuneKv4Paired);
+    if (tune_paired == "0") p.paired = false;
+    else if (tune_paired == "1") p.paired = can_pair;
     if (p.paired) {
         p.grid = (B + 1) / 2 * Hkv;
         p.waves = 8;

@@ -262,7 +262,9 @@ qoq_status qoq_w4a8_linear(const uint16_t* x, int64_t M, int64_t K,
  *                 (nothing launched).
  *   "variant"     comparison GEMMs (qoq_variants.h): "MT,CB,PB,WGPERCU,NW".
  *   "kv4_splits"  decode attention (qoq_kv4.h): split count n > 0 (<= 65536).
- *   "kv4_paired"  decode attention: "0" turns the paired schedule off.
+ *   "kv4_paired"  decode attention: "0" turns the paired schedule off, "1"
+ *                 takes it whenever the batch allows it (by default only for
+ *                 contexts of 1024 tokens or more).
  * Settings apply to calls made after this one returns; setting a key while
  * another thread enqueues work races with that thread's plan.
  * Errors: QOQ_ERR_NULL (key NULL), QOQ_ERR_CONFIG (unknown key). */

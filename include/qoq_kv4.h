@@ -78,7 +78,8 @@ size_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int
  * the lengths (sets how contexts are split), out [B, H, D] fp16.
  * H % H_kv == 0 and H / H_kv <= 16. The "kv4_splits" key of
  * qoq_set_tuning forces n splits (at most 65536), "kv4_paired" = "0" turns
- * the paired schedule off. QOQ_ERR_SHAPE also when a launch would count 2^32
+ * the paired schedule off, "1" forces it where the batch allows it.
+ * QOQ_ERR_SHAPE also when a launch would count 2^32
  * work-items or more (B * H >= 2^26, or a forced split count that large).
  * Errors: QOQ_ERR_NULL, QOQ_ERR_SHAPE, QOQ_ERR_ALIGN, QOQ_ERR_WORKSPACE,
  * QOQ_ERR_HIP. */

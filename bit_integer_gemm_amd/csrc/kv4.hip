@@ -252,6 +252,15 @@ __device__ __forceinline__ v8h join(const h2 (&r)[4]) {
     return o;
 }
 
+// fp32 x times the fp16 in the low (HI = false) or high half of w, one
+// rounding: an FMA with a +0 addend on the converted half, which the
+// compiler issues as one mixed-precision FMA (no conversion instruction)
+template <bool HI>
+__device__ __forceinline__ float mul_f16(float x, uint32_t w) {
+    const h2 v = __builtin_bit_cast(h2, w);
+    return __builtin_fmaf(x, float(v[HI ? 1 : 0]), 0.0f);
+}
+
 // Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
 // that hold one query's scores) with gfx950's row swaps: swapping the upper
 // 32 lanes of one copy with the lower 32 of another leaves x[l] and
@@ -459,7 +468,9 @@ kv4_attention_kernel(AttnArgs a) {
     const uint32_t e64 = __builtin_amdgcn_readfirstlane(0x64006400u);
     // online softmax for query j over a block's 32 tokens; the accumulators
     // are rescaled only when the running maximum grows by more than 2^8
-    // (probabilities stay below 256 in between). Returns the fp16 P operand.
+    // (probabilities stay below 256 in between). The maximum is one of the
+    // scores, so its token's probability is exactly 1. Returns the fp16 P
+    // operand.
     auto softmax = [&](const float (&zs)[8]) {
         float bm = zs[0];
 #pragma unroll
@@ -523,13 +534,11 @@ kv4_attention_kernel(AttnArgs a) {
             return tbase + tok < len;
         };
         const uint32_t skw[4] = {r.sk.x, r.sk.y, r.sk.z, r.sk.w};
-        // value zeros of the lane's tokens e = 0..3, 4..7 (zero bytes hold
-        // z_k | z_v << 4)
-        const uint32_t zv03 = (r.z.x >> 4) & 0x0f0f0f0fu, zv47 = (r.z.y >> 4) & 0x0f0f0f0fu;
         // scores: S[token, query] = q~ . (u - z_k). The key codes enter the
         // MFMA as the fp16 subnormals u 2^-24 (their bit patterns, exact),
-        // the zero point through the fifth MFMA; the sum is 2^-24-scaled
-        // fp32, undone together with the scale s_k and log2(e) / sqrt(D).
+        // the zero point through the fifth MFMA; the sum times the token's
+        // scale s_k (one mixed-precision multiply) is the 2^-24-scaled
+        // score, then brought to the log2 domain (2^24 log2(e) / sqrt(D)).
         float zs[8];
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -546,27 +555,30 @@ kv4_attention_kernel(AttnArgs a) {
             const uint4 zrow = uint4{zt * 0x00800080u, zt << 7, 0u, 0u};
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, zrow), qz, acc, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * tile + i;
-                const h2 sk2 = __builtin_bit_cast(h2, skw[e >> 1]);
-                zs[e] = acc[i] * (float(sk2[e & 1]) * kS24);
+            for (int i = 0; i < 4; i += 2) {
+                zs[4 * tile + i] = mul_f16<false>(acc[i], skw[2 * tile + i / 2]) * kS24;
+                zs[4 * tile + i + 1] = mul_f16<true>(acc[i + 1], skw[2 * tile + i / 2]) * kS24;
             }
         }
-        uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+        uint32_t svw[4] = {r.sv.x, r.sv.y, r.sv.z, r.sv.w};
         if (partial) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) zs[e] = valid(e) ? zs[e] : -INFINITY;
+            // tokens past the context get value scale 0, whatever bits
+            // their slot holds
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr)
-                keep[pr] = (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
+                svw[pr] &= (valid(2 * pr) ? 0x0000ffffu : 0u) | (valid(2 * pr + 1) ? 0xffff0000u : 0u);
         }
         const v8h pop = softmax(zs);
         // values: sum_t p_t s_t (u_t - z_t). The token's scale rides on its
-        // probability, P' = fp16(fp16(p) s) (tokens past the context get
-        // scale 0, whatever bits their slot holds), and the value operand is
-        // the exact integer (1024 + u) - (1024 + z) = u - z: one packed
-        // subtraction per two values, no per-value scaling.
-        const uint32_t svw[4] = {r.sv.x, r.sv.y, r.sv.z, r.sv.w};
+        // probability, P' = fp16(fp16(p) s), and the value operand is the
+        // exact integer (1024 + u) - (1024 + z) = u - z: one packed
+        // subtraction per two values, no per-value scaling. (Codes and zeros
+        // in separate MFMA sums would save the subtractions but not the
+        // accuracy: the two sums cancel where u ~ z, and their rounding then
+        // exceeds the error bound of the exact difference.)
+        const uint32_t zv03 = (r.z.x >> 4) & 0x0f0f0f0fu, zv47 = (r.z.y >> 4) & 0x0f0f0f0fu;
         // 1024 + z_v pairs: the zero bytes with 0x64 exponent bytes between
         h2 zz[4];
         zz[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(c64, zv03, 0x04010400u));
@@ -576,7 +588,7 @@ kv4_attention_kernel(AttnArgs a) {
         v8h pv;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const h2 ps = h2{pop[2 * pr], pop[2 * pr + 1]} * __builtin_bit_cast(h2, svw[pr] & keep[pr]);
+            const h2 ps = h2{pop[2 * pr], pop[2 * pr + 1]} * __builtin_bit_cast(h2, svw[pr]);
             pv[2 * pr] = ps[0];
             pv[2 * pr + 1] = ps[1];
         }

@@ -671,16 +671,13 @@ kv4_attention_kernel(AttnArgs a) {
     // rounds end and are only computed. Every step issues its load (indices
     // past the wave's last are clamped to it: cache hits, never used), and
     // each block's loads stay together and in order (scheduling barriers),
-    // so each compute waits for exactly its own block.
-    auto block_loop = [&](int first, int last, auto load_at, auto compute_at) {
+    // so each compute waits for exactly its own block. The caller has
+    // already loaded ring[0] with block `first` (issued before the query
+    // loads, so the two latencies overlap).
+    static_assert(R == 2, "ring[0] is the caller's prologue load");
+    auto block_loop = [&](Blk4 (&ring)[R], int first, int last, auto load_at, auto compute_at) {
         if (first > last) return;
-        Blk4 ring[R];
         const int mine = (last - first) / NW + 1;   // blocks of this wave
-#pragma unroll
-        for (int s = 0; s < R - 1; ++s) {
-            load_at(ring[s], min(first + s * NW, last));
-            __builtin_amdgcn_sched_barrier(0);
-        }
         int b = first, i = 0;
         for (; i + R <= mine; i += R) {
 #pragma unroll
@@ -701,18 +698,15 @@ kv4_attention_kernel(AttnArgs a) {
   auto run = [&](const int b_in, const int h, const int sp) {
     // b comes from LDS in the paired schedule: the same in every lane
     const int b = __builtin_amdgcn_readfirstlane(b_in);
-    len = __builtin_amdgcn_readfirstlane(clamped_len(b));
-    const int nb = (len + kBlk - 1) / kBlk;
     const int blk0 = sp * a.bps;
-    const int blk1 = min(nb, blk0 + a.bps);
-    // a split past the end of its context writes nothing: the merge of the
-    // splits reads only those that hold tokens
-    if (a.splits > 1 && blk0 >= nb) return;
-    set_query(b, h, qop, qsum);
-    qz = make_qz(qsum);
-    reset();
     const int first = blk0 + wave;
     if constexpr (kF16) {
+        len = __builtin_amdgcn_readfirstlane(clamped_len(b));
+        const int nb = (len + kBlk - 1) / kBlk;
+        const int blk1 = min(nb, blk0 + a.bps);
+        if (a.splits > 1 && blk0 >= nb) return;
+        set_query(b, h, qop, qsum);
+        reset();
         // the fp16 cache (comparison point): two blocks, the next one's
         // loads in flight while one is computed
         const uint8_t* rg = region_base(b, h);
@@ -727,8 +721,22 @@ kv4_attention_kernel(AttnArgs a) {
             compute16(rb, bi + NW);
         }
     } else {
+        // the wave's first block, the query and the length all at once: the
+        // block needs no length (a block of the region's capacity, clamped;
+        // unused when the context ends before it)
         const Rs rs = region_rsrc(b, h);
-        block_loop(first, blk1 - 1, [&](Blk4& r, int blk) { load4(r, rs, blk); },
+        Blk4 ring[R];
+        load4(ring[0], rs, min(first, int(nblk) - 1));
+        set_query(b, h, qop, qsum);
+        len = __builtin_amdgcn_readfirstlane(clamped_len(b));
+        const int nb = (len + kBlk - 1) / kBlk;
+        const int blk1 = min(nb, blk0 + a.bps);
+        // a split past the end of its context writes nothing: the merge of
+        // the splits reads only those that hold tokens
+        if (a.splits > 1 && blk0 >= nb) return;
+        qz = make_qz(qsum);
+        reset();
+        block_loop(ring, first, blk1 - 1, [&](Blk4& r, int blk) { load4(r, rs, blk); },
                    [&](const Blk4& r, int blk) { compute4(r, blk); });
     }
     flush(0);
@@ -739,17 +747,27 @@ kv4_attention_kernel(AttnArgs a) {
   // the paired schedule's two contexts (A, then B; bB == bA: A alone) as one
   // stream of blocks over the workgroup's waves: a wave whose blocks cross
   // from A to B parks its A state in slot 0 and goes on with B's query;
-  // both merges run at the end, on the two halves of the workgroup
-  auto run_pair = [&](const int bA_in, const int bB_in, const int h) {
+  // both merges run at the end, on the two halves of the workgroup. The
+  // lengths come from the ranking in LDS.
+  auto run_pair = [&](const int bA_in, const int bB_in, const int lenA_in, const int lenB_in,
+                      const int h) {
     const int bA = __builtin_amdgcn_readfirstlane(bA_in);
     const int bB = __builtin_amdgcn_readfirstlane(bB_in);
     const bool alone = bA == bB;
-    const int lenA = __builtin_amdgcn_readfirstlane(clamped_len(bA));
-    const int lenB = alone ? 0 : __builtin_amdgcn_readfirstlane(clamped_len(bB));
+    const int lenA = __builtin_amdgcn_readfirstlane(lenA_in);
+    const int lenB = alone ? 0 : __builtin_amdgcn_readfirstlane(lenB_in);
     const int nA = (lenA + kBlk - 1) / kBlk;
     const int nB = (lenB + kBlk - 1) / kBlk;
     const Rs rsA = region_rsrc(bA, h);
     const Rs rsB = region_rsrc(bB, h);
+    auto load_at = [&](Blk4& r, int c) {
+        if (c < nA) load4(r, rsA, c);
+        else load4(r, rsB, c - nA);
+    };
+    // the wave's first block before the queries (clamped to the stream's
+    // last, or block 0 of B when the pair holds no tokens: unused then)
+    Blk4 ring[R];
+    load_at(ring[0], min(wave, max(nA + nB - 1, 0)));
     v8h qopB[4];
     float qsumB;
     set_query(bB, h, qopB, qsumB);
@@ -760,11 +778,7 @@ kv4_attention_kernel(AttnArgs a) {
     reset();
     bool inB = false;
     block_loop(
-        wave, nA + nB - 1,
-        [&](Blk4& r, int c) {
-            if (c < nA) load4(r, rsA, c);
-            else load4(r, rsB, c - nA);
-        },
+        ring, wave, nA + nB - 1, load_at,
         [&](const Blk4& r, int c) {
             if (c >= nA && !inB) {
                 flush(0);
@@ -819,7 +833,8 @@ kv4_attention_kernel(AttnArgs a) {
     const int p = blockIdx.x / a.Hkv;
     const int h = blockIdx.x % a.Hkv;
     if constexpr (kPairStream) {
-        run_pair(by_rank[p], by_rank[a.B - 1 - p], h);
+        const int bA = by_rank[p], bB = by_rank[a.B - 1 - p];
+        run_pair(bA, bB, rank_len[bA], rank_len[bB], h);
     } else {
         run(by_rank[p], h, 0);
         if (a.B - 1 - p != p) {

@@ -188,6 +188,7 @@ def test_attention_parity(B, H, Hkv, lens, C, monkeypatch):
     (5, 8, 2, [40, 128, 3, 128, 77], 128),     # odd batch (the middle rank runs alone), a tie
     (6, 4, 1, [0, 96, 1, 64, 95, 96], 96),      # empty context, ties, one-token context
     (2, 32, 8, [128, 17], 128),                 # one pair
+    (4, 8, 2, [0, 0, 0, 1200], 1216),           # a pair of two empty contexts
 ])
 def test_paired_schedule(B, H, Hkv, lens, C, paired, monkeypatch):
     """Unsplit batches of 2..256 sequences whose pairs fit one per CU run two

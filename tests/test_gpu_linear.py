@@ -20,7 +20,7 @@ DEV = "cuda:0"
 
 # (M, K, N): one to sixteen tokens, group counts that do and do not fill the
 # waves, column counts that fill no tile
-FUSED = [(1, 128, 16), (1, 4096, 4096), (5, 640, 208), (8, 1152, 400), (8, 8192, 528),
+FUSED = [(1, 128, 16), (1, 4096, 4096), (8, 4096, 4096), (5, 640, 208), (8, 1152, 400), (8, 8192, 528),
          (3, 2048, 1040), (4, 512, 512), (2, 384, 48),
          # 5-12 tokens with two column blocks per workgroup (more than 16e6
          # values quantized, or 9-12 tokens past 4096 columns; odd block

@@ -288,16 +288,29 @@ def test_workspace_is_reusable(monkeypatch):
         check_y(y.cpu().numpy().astype(np.float64), oracle.epilogue(acc_ref, sx_ref, q["s1"]))
 
 
-def test_prefill_full_size_all_outputs(monkeypatch):
-    """The 4096-token prefill workload (M = 4096, K = 4096, N = 14336) in the
-    benchmark's launch configuration, every one of its 58.7 M outputs: the
-    INT32 accumulators bit-exact against the oracle's exact GEMM (fp64 BLAS
-    on the integer codes, exact below 2^53) and y within the tolerance."""
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+CASES = [(key, shape.name, M) for key in wl.ORDER[1:] for shape in wl.WORKLOADS[key].shapes
+         for M in wl.WORKLOADS[key].Ms]
+COMMON_TILE_CASES = {("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),
+                     ("qwen15_72b", "gate_up", 1024), ("qwen15_72b", "down", 1024)}
+
+
+@pytest.mark.parametrize("key,shape_name,M", CASES, ids=[f"{k}-{s}-M{m}" for k, s, m in CASES])
+def test_workload_full_size_all_outputs(key, shape_name, M, monkeypatch):
+    """Every benchmarked layer at full size under the GEMM's default plan
+    (the decode, shared-activation, K-split, 32x32 and wide tile families,
+    K split into ranges through the workspace where the plan does; the 1-
+    and 8-token decode layers also run fused, tests/test_gpu_linear.py),
+    every output: the INT32 accumulators bit-exact against the oracle's
+    exact GEMM (fp64 BLAS on the integer codes, exact below 2^53) and y
+    within the tolerance."""
+    w = wl.WORKLOADS[key]
+    shape = next(s for s in w.shapes if s.name == shape_name)
     qoq.set_tuning("gemm", None)
-    w = wl.WORKLOADS["prefill"]
-    shape = w.shapes[0]
-    M = w.Ms[0]
-    _announce("prefill all outputs", M, shape.K, shape.N)
+    split = qoq.qoq_gemm_workspace_bytes(M, shape.N, shape.K) > 0
+    _announce("all outputs", key, shape_name, M, shape.K, shape.N, "split K" if split else "")
     W, X, _ = wl.make_case(w, shape, M)
     pw, x8, s_x, y, acc = gpu_run(W, X, canonical=False)
     q = oracle.quantize_weights(W)
@@ -313,13 +326,13 @@ def test_prefill_full_size_all_outputs(monkeypatch):
     print(f"[gpu-case] ok, all {M * shape.N} outputs, max rel err {err:.2e}", flush=True)
 
 
-# ---------------------------------------------------------------------------
-# the workloads at full size
-# ---------------------------------------------------------------------------
-CASES = [(key, shape.name, M) for key in wl.ORDER[1:] for shape in wl.WORKLOADS[key].shapes
-         for M in wl.WORKLOADS[key].Ms]
-COMMON_TILE_CASES = {("llama3_8b", "qkv", 256), ("llama3_8b", "gate_up", 256), ("prefill", "prefill", 4096),
-                     ("qwen15_72b", "gate_up", 1024), ("qwen15_72b", "down", 1024)}
+def test_split_k_plans_among_the_workloads():
+    """The all-outputs cases include split-K plans (partial sums through the
+    workspace and the split-K epilogue kernel)."""
+    split = [(k, s, m) for k, s, m in CASES
+             if qoq.qoq_gemm_workspace_bytes(m, next(x for x in wl.WORKLOADS[k].shapes if x.name == s).N,
+                                             next(x for x in wl.WORKLOADS[k].shapes if x.name == s).K) > 0]
+    assert ("qwen15_72b", "down", 1024) in split and ("qwen15_72b", "down", 64) in split, split
 
 
 @pytest.mark.parametrize("key,shape_name,M", CASES, ids=[f"{k}-{s}-M{m}" for k, s, m in CASES])

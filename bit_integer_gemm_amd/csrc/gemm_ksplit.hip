@@ -28,7 +28,12 @@
 namespace qoq {
 namespace {
 
-template <int MT, int CB, int KW, int PD>
+// Record chunks (8 groups each) a wave stages in LDS; a range of up to
+// kRecLdsMaxGroups groups starting anywhere spans at most that many.
+constexpr int kRecLdsChunks = 8;
+constexpr int kRecLdsMaxGroups = 8 * kRecLdsChunks - 7;
+
+template <int MT, int CB, int KW, int PD, bool RL>
 __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
     const int8_t* __restrict__ x8, const float* __restrict__ s_x, int M, int K,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rec, int ng8,
@@ -39,7 +44,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
     // the upper half of the waves first folds into the lower half
     constexpr int KR = KW * T * 4096 <= 128 * 1024 ? KW : KW / 2;
     static_assert(KR * T * 4096 <= 128 * 1024, "LDS reduction buffer above 128 KiB");
-    __shared__ int red[KR * T * 16 * 64];
+    // RL: the group records of each wave's range staged in LDS (CB tiles x
+    // 2 blocks x 8 record chunks of 256 bytes per wave), sharing the space
+    // of the cross-wave sum, which only starts after every wave's loop
+    constexpr int kRedInts = KR * T * 16 * 64;
+    constexpr int kRecWaveU16 = CB * 2 * kRecLdsChunks * 128;
+    constexpr int kRecInts = RL ? KW * kRecWaveU16 / 2 : 0;
+    __shared__ __attribute__((aligned(16))) int red[kRedInts > kRecInts ? kRedInts : kRecInts];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31;
@@ -82,6 +93,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
         b_off[cb] = blk * ng * kBlockBytes + (c + 16 * q) * 16;
         r_off[cb] = (blk * ng8 * kBlockCols + c) * (kRecChunk * 2);
     }
+    // RL: this wave's records in LDS, [cb][block of the tile][chunk - c0]
+    // [channel][group % 8]; lane (j, q) reads its channel's entry
+    uint16_t* rl = reinterpret_cast<uint16_t*>(red) + wave * kRecWaveU16;
+    const int c0 = gb >> 3;
+    auto rec_lds = [&](int cb, int g) {
+        return uint32_t(rl[((cb * 2 + (j >> 4)) * kRecLdsChunks + (g >> 3) - c0) * 128 + c * 8 + (g & 7)]);
+    };
 
     v16i acc[MT][CB];
 #pragma unroll
@@ -121,9 +139,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
     // on the INT8 weights of buffer i % 2, the VALU turns the packed codes of
     // group i + 1 into buffer (i + 1) % 2, interleaved one MFMA to a few
     // VALU instructions, so the SIMD's matrix pipe and VALU work at once.
+    // Records: without RL each stage also carries its groups' 2-byte records,
+    // loaded from global memory beside the codes (a vector-memory request per
+    // record: measured at 9-10 % of the operand stream's time); with RL they
+    // are read from LDS two groups ahead into a pair of registers.
     v4i av[PD][MT][4];
     uint4 qn[PD][CB][2];
-    uint32_t rs[PD][CB];
+    uint32_t rs[RL ? 2 : PD][CB];
     v4i bq[2][CB][4];
     auto load = [&](int p, int g) {
 #pragma unroll
@@ -132,8 +154,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
                 rb, b_off[cb], g * kBlockBytes, 0));
             qn[p][cb][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rb, b_off[cb], g * kBlockBytes + 512, 0));
-            rs[p][cb] = __builtin_amdgcn_raw_buffer_load_b16(
-                rr, r_off[cb], (g >> 3) * kRecChunkBytes + (g & 7) * 2, 0);
+            if constexpr (!RL)
+                rs[p][cb] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rr, r_off[cb], (g >> 3) * kRecChunkBytes + (g & 7) * 2, 0);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -142,12 +165,17 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
                 av[p][mt][st] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                     ra, a_off[mt], g * kActGroupBytes + 2 * kActUnit * st, 0));
     };
-    auto dequant = [&](int b, int p) {
+    // dequantize stage p's codes into buffer b with record set r
+    auto dequant = [&](int b, int p, int r) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            dequant_block(qn[p][cb][0], rs[p][cb], bq[b][cb][0], bq[b][cb][2]);
-            dequant_block(qn[p][cb][1], rs[p][cb], bq[b][cb][1], bq[b][cb][3]);
+            dequant_block(qn[p][cb][0], rs[r][cb], bq[b][cb][0], bq[b][cb][2]);
+            dequant_block(qn[p][cb][1], rs[r][cb], bq[b][cb][1], bq[b][cb][3]);
         }
+    };
+    auto read_rec = [&](int r, int g) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) rs[r][cb] = rec_lds(cb, g);
     };
     constexpr int kMfma = 4 * MT * CB;            // MFMAs per group
     constexpr int kValu = 62 * CB;                // dequantization VALU per group (about)
@@ -171,8 +199,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
     auto step = [&](int i, int u, bool full) {
         const int p = u % PD, pn = (u + 1) % PD, b = u & 1;
         if (full || i < cnt) {
+            // RL: the records of group i + 2 into the pair entry group i used
+            if constexpr (RL) read_rec(b, gb + min(i + 2, cnt - 1));
             mfmas(b, p);
-            if (full || i + 1 < cnt) dequant(b ^ 1, pn);
+            if (full || i + 1 < cnt) dequant(b ^ 1, pn, RL ? b ^ 1 : pn);
 #pragma unroll
             for (int k = 0; k < kMfma; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
@@ -185,10 +215,45 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
     };
     constexpr int U = PD % 2 == 0 ? PD : 2 * PD;
     if (cnt > 0) {
+        uint4 stg[CB][2][2];
+        if constexpr (RL) {
+            // the range's record chunks c0 .. c0 + 7 (clamped) of the 2 CB
+            // blocks: lane l takes 16 bytes of chunk c0 + l / 16 + 4 k
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int blk = min(nb0 + 2 * cb + h2, nbt - 1);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const int ch = min(c0 + (lane >> 4) + 4 * k, ng8 - 1);
+                        stg[cb][h2][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                            rr, (blk * ng8 + ch) * kRecChunkBytes + (lane & 15) * 16, 0, 0));
+                    }
+                }
+        }
 #pragma unroll
         for (int p = 0; p < PD; ++p) load(p, gb + min(p, cnt - 1));
         __builtin_amdgcn_sched_barrier(0);
-        dequant(0, 0);
+        if constexpr (RL) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        *reinterpret_cast<uint4*>(rl + ((cb * 2 + h2) * kRecLdsChunks + (lane >> 4) + 4 * k) * 128 +
+                                                  (lane & 15) * 8) = stg[cb][h2][k];
+            // written by other lanes of this wave: order the wave's LDS
+            // accesses (DS instructions of one wave complete in order)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            read_rec(0, gb);
+            read_rec(1, gb + min(1, cnt - 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dequant(0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         int i0 = 0;
         for (; i0 + U <= cnt; i0 += U) {
@@ -200,6 +265,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
             for (int u = 0; u < U; ++u) step(i0 + u, u, false);
         }
     }
+
+    // RL: no wave may still read its records when the sum below reuses them
+    if constexpr (RL) __syncthreads();
 
     // Add the KW partial tiles in LDS: wave w stores register r of tile t at
     // red[((w T + t) 16 + r) 64 + lane] (conflict-free), then each thread
@@ -270,8 +338,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_ksplit32_kernel(
 
 template <int MT, int CB, int KW, int PD>
 hipError_t launch_one(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-    return launch_kernel(gemm_ksplit32_kernel<MT, CB, KW, PD>, dim3(p.grid_x), dim3(64 * KW), 0,
-                         stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
+    // records in LDS when every wave's group range fits the staging area
+    const int gpw = ((a.K >> 7) + KW - 1) / KW;
+    if (gpw <= kRecLdsMaxGroups)
+        return launch_kernel(gemm_ksplit32_kernel<MT, CB, KW, PD, true>, dim3(p.grid_x),
+                             dim3(64 * KW), 0, stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8,
+                             a.s1, a.N, a.y, a.acc_debug);
+    return launch_kernel(gemm_ksplit32_kernel<MT, CB, KW, PD, false>, dim3(p.grid_x), dim3(64 * KW),
+                         0, stream, a.x8, a.s_x, a.M, a.K, a.nib, a.rec, a.ng8, a.s1, a.N, a.y,
                          a.acc_debug);
 }
 

@@ -319,6 +319,23 @@ def test_ksplit32_family(monkeypatch, cfg):
         _run(monkeypatch, _fmt("ksplit", cfg), M, K, N)
 
 
+# The K-split kernel reads a wave's group records into LDS once when the
+# wave's K range has at most 57 groups (8 chunks of 8 groups, the range
+# starting anywhere in its first chunk) and per group otherwise. Random
+# weights (every group its own record) on both sides of that limit, with
+# the waves' ranges starting at every offset inside a chunk (57 w mod 8 for
+# w = 0..7: 0, 1, ..., 7).
+KSPLIT_RECORD_LIMIT = [((2, 2, 4, 3), 4 * 57 * 128), ((2, 2, 4, 3), 4 * 58 * 128),
+                       ((2, 1, 8, 2), 8 * 57 * 128), ((2, 1, 8, 2), 8 * 58 * 128),
+                       ((1, 3, 8, 2), 8 * 57 * 128)]
+
+
+@pytest.mark.parametrize("cfg,K", KSPLIT_RECORD_LIMIT,
+                         ids=[f"{_fmt('ksplit', c)}@K{k}" for c, k in KSPLIT_RECORD_LIMIT])
+def test_ksplit32_records_at_the_staging_limit(monkeypatch, cfg, K):
+    _run(monkeypatch, _fmt("ksplit", cfg), 37, K, 208)
+
+
 @pytest.mark.parametrize("cfg", WIDE, ids=[_fmt("wide", c) for c in WIDE])
 def test_wide_family(monkeypatch, cfg):
     for (M, K, N) in SHAPES_LARGE_M + SHAPES_SMALL_M[1:2]:

@@ -275,6 +275,17 @@ def test_split_k(monkeypatch, fam, cfg, splits):
         _run(monkeypatch, name, M, K, N)
 
 
+@pytest.mark.parametrize("K", [10240, 17408])
+def test_split_k_more_than_eight_partials(monkeypatch, K):
+    """The second kernel adds the partials in batches of 8: 10 and 17 of them
+    (8-group splits of 80 and 136 groups) take two and three batches, the
+    last one short."""
+    name = "lds,2,1,8,2,64"
+    qoq.set_tuning("gemm", name)
+    assert qoq.qoq_gemm_workspace_bytes(37, 208, K) == (K // 1024) * 37 * 208 * 4
+    _run(monkeypatch, name, 37, K, 208)
+
+
 def test_split_k_needs_its_workspace(monkeypatch):
     pw, x8, s_x, _ = _case(64, 2560, 528)
     qoq.set_tuning("gemm", "lds,4,1,4,2,3")

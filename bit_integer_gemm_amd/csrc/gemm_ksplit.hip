@@ -10,9 +10,12 @@
 //
 // Work split: a workgroup owns a (32 MT) x (32 CB) output tile and all of K;
 // its KW waves take contiguous ranges of the 128-input groups and each keeps
-// PD groups of activation fragments, packed weights and group records in
-// flight in a register ring (loaded straight from global memory: nothing is
-// shared between the waves, so there is no barrier in the main loop). The
+// PD groups of activation fragments and packed weights in flight in a
+// register ring (loaded straight from global memory: nothing is shared
+// between the waves, so there is no barrier in the main loop). A wave reads
+// the group records of its whole range into its own LDS area once, with
+// 16-byte loads, when the range spans at most 8 record chunks; longer ranges
+// carry one 2-byte record load per group in the ring. The
 // KW partial INT32 tiles are added in LDS (integer addition: the sum is the
 // same in any order) and the epilogue writes the tile. Compared with the
 // 16-row decode family this issues the full-rate 32x32x32 INT8 MFMA and
